@@ -1,0 +1,118 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared symbol, and
+validates arguments on the host before any launch (no GPU needed for any of these)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import w4a4_integer_quantized_amd as rq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "convrot.h")
+
+A = 0x10000          # fake, 16-byte aligned "device addresses": only compared, never touched
+GB = 1 << 30
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(rq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = rq.load()
+    names = declared_symbols()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.rq_version().decode().count(".") == 2
+
+
+def test_status_strings():
+    for s in range(5):
+        assert rq.rq_status_string(s).startswith("RQ_")
+
+
+def _args(**kw):
+    cfg = rq.make_cfg(kw.pop("bits", 8), kw.pop("rot", 128), kw.pop("kind", rq.RQ_ROT_WHT))
+    M, K, N = kw.pop("M", 256), kw.pop("K", 1024), kw.pop("N", 1024)
+    base = dict(X=A, x_dtype=rq.RQ_F16, M=M, K=K, Wq=A + 4 * GB, w_scale=A + 8 * GB, N=N,
+                bias=A + 9 * GB, cfg=cfg, Y=A + 12 * GB, ws=A + 20 * GB,
+                ws_bytes=rq.rq_rotq_linear_workspace_size(M, K, cfg))
+    base.update(kw)
+    return base
+
+
+def check(**kw):
+    a = _args(**kw)
+    return rq.rq_check_rotq_linear_args(a["X"], a["x_dtype"], a["M"], a["K"], a["Wq"], a["w_scale"],
+                                        a["N"], a["bias"], a["cfg"], a["Y"], a["ws"], a["ws_bytes"])
+
+
+def test_valid_arguments_pass():
+    assert check() == rq.RQ_OK
+    assert check(bias=None) == rq.RQ_OK
+    assert check(M=0) == rq.RQ_OK
+    assert check(bits=4, K=4096) == rq.RQ_OK
+    assert check(x_dtype=rq.RQ_BF16, K=1536, N=4608) == rq.RQ_OK
+    assert check(M=41472, K=1024, N=3072) == rq.RQ_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), rq.RQ_EINVAL),
+    (dict(Y=None), rq.RQ_EINVAL),
+    (dict(Wq=A + 4 * GB + 8), rq.RQ_EINVAL),                 # misaligned
+    (dict(w_scale=None), rq.RQ_EINVAL),
+    (dict(M=-1), rq.RQ_EINVAL),
+    (dict(x_dtype=7), rq.RQ_EINVAL),
+    (dict(x_dtype=rq.RQ_F32), rq.RQ_EUNSUPPORTED),
+    (dict(K=1000), rq.RQ_EUNSUPPORTED),
+    (dict(K=64), rq.RQ_EUNSUPPORTED),
+    (dict(K=131072 + 128), rq.RQ_EUNSUPPORTED),
+    (dict(N=1000), rq.RQ_EUNSUPPORTED),
+    (dict(N=0), rq.RQ_EUNSUPPORTED),
+    (dict(bits=6), rq.RQ_EUNSUPPORTED),
+    (dict(bits=4, K=384), rq.RQ_EUNSUPPORTED),                # 4-bit GEMM needs K % 256 == 0
+    (dict(rot=64), rq.RQ_EUNSUPPORTED),
+    (dict(kind=0), rq.RQ_EUNSUPPORTED),
+    (dict(ws_bytes=100), rq.RQ_EWORKSPACE),
+    (dict(Y=A + 100 * 2), rq.RQ_EINVAL),                      # Y overlaps X
+    (dict(ws=A + 12 * GB + 4096), rq.RQ_EINVAL),              # workspace overlaps Y
+    (dict(ws=A + 64), rq.RQ_EINVAL),                          # workspace overlaps X
+])
+def test_invalid_arguments_rejected(kw, status):
+    assert check(**kw) == status
+    assert rq.load().rq_last_error_detail().decode()
+
+
+def test_workspace_size():
+    cfg8, cfg4 = rq.make_cfg(8), rq.make_cfg(4)
+    assert rq.rq_rotq_linear_workspace_size(256, 1024, cfg8) == 256 * 1024 + 1024
+    assert rq.rq_rotq_linear_workspace_size(5184, 4096, cfg4) == 5184 * 2048 + 5184 * 4
+    assert rq.rq_rotq_linear_workspace_size(5, 256, cfg4) == 768 + 256
+    assert rq.rq_rotq_linear_workspace_size(3, 128, cfg8) == 512 + 256
+    assert rq.rq_rotq_linear_workspace_size(3, 128, rq.make_cfg(5)) == 0
+
+
+def test_entry_points_reject_before_launch():
+    # Invalid calls must return a status without touching the (absent) GPU.
+    cfg = rq.make_cfg(8)
+    assert rq.rq_quantize_weights(A, rq.RQ_F32, 16, 100, cfg, A + GB, A + 2 * GB, None) == rq.RQ_EUNSUPPORTED
+    assert rq.rq_rotate_quantize(A, 9, 16, 128, cfg, A + GB, A + 2 * GB, None) == rq.RQ_EINVAL
+    assert rq.rq_rotate_quantize(A, rq.RQ_F16, 16, 128, cfg, A + 8, A + 2 * GB, None) == rq.RQ_EINVAL  # overlap
+    assert rq.rq_gemm_dequant(A, A + GB, A + 2 * GB, A + 3 * GB, None, 16, 24, 128, cfg, A + 4 * GB,
+                              rq.RQ_F16, None) == rq.RQ_EUNSUPPORTED   # N % 16
+    assert rq.rq_gemm_dequant(A, A + GB, A + 2 * GB, A + 3 * GB, None, 16, 32, 128, cfg, A + 4 * GB,
+                              rq.RQ_F32, None) == rq.RQ_EUNSUPPORTED   # f32 output
+    assert rq.rq_gemm_s32(A, A + GB, 16, 32, 128, rq.make_cfg(3), A + 2 * GB, None) == rq.RQ_EUNSUPPORTED
+    assert rq.rq_gemm_s32(A, A + GB, 16, 32, 128, cfg, A + 8, None) == rq.RQ_EINVAL     # misaligned/overlap
+    # M == 0 is a no-op that succeeds without launching anything
+    assert rq.rq_gemm_s32(A, A + GB, 0, 32, 128, cfg, A + 2 * GB, None) == rq.RQ_OK
+    assert rq.rq_rotate_quantize(A, rq.RQ_F16, 0, 128, cfg, A + GB, A + 2 * GB, None) == rq.RQ_OK
+
+
+def test_tensor_wrappers_refuse_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        rq.rotate_quantize(torch.zeros(4, 128, dtype=torch.float16))

@@ -1,0 +1,191 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle, element by element.
+
+Bar: codes, scales and int32 accumulators bit-exact (a code may differ only if its
+pre-rounding value lies within one fp32 ulp of a .5 boundary, at most 1e-5 of codes);
+fp16 / bf16 outputs within max|err| <= 1e-3 + 2^-9 |ref| -- and, because the kernels follow
+the same fp32 operation order as the oracle, bit-identical as well.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import w4a4_integer_quantized_amd as rq
+from w4a4_integer_quantized_amd import synth
+from tests.gpu_util import (IO_CODE, bits_from_dev, codes_np, compare_codes, dev_from_bits,
+                            need_gpu, y_tolerance_ok)
+
+pytestmark = pytest.mark.gpu
+
+
+def _rows(seed, M, K, io, zero_rows=(), dist="normal"):
+    rng = np.random.default_rng(seed)
+    x = synth.random_rows(rng, M, K, dist, max(1, K // 100), 40.0)
+    for r in zero_rows:
+        if r < M:
+            x[r] = 0
+    if io == "f32":
+        return x, x
+    return synth.to_io_bits(x, io), None
+
+
+# (K, M) pairs cover every kernel shape: T = 16/32/64/128/256 threads per row, P = 1..8
+# pieces, and the generic two-pass kernel (K = 2176, 17 blocks); M spans ragged tails.
+RQ_CASES = [(128, 1), (128, 37), (256, 5), (384, 33), (640, 9), (1024, 300), (1536, 129),
+            (2176, 11), (4096, 70), (6144, 19), (8192, 6), (16384, 3)]
+
+
+@pytest.mark.parametrize("K,M", RQ_CASES)
+@pytest.mark.parametrize("io,bits", [("f16", 8), ("bf16", 8), ("f16", 4), ("f32", 8), ("f32", 4)])
+def test_rotate_quantize_parity(K, M, io, bits):
+    need_gpu()
+    xb, _ = _rows(K + M + bits, M, K, io, zero_rows=(0, M - 1) if M > 2 else ())
+    Xd = dev_from_bits(xb, io)
+    Xq, xs = rq.rotate_quantize(Xd, bits=bits)
+    torch.cuda.synchronize()
+    ref_c, ref_s, ref_p = oracle.quantize_rows(xb, IO_CODE[io], bits, want_pre=True)
+    compare_codes(codes_np(Xq), ref_c, ref_p, bits, K)
+    assert np.array_equal(xs.cpu().numpy().view(np.uint32), ref_s.view(np.uint32))
+
+
+@pytest.mark.parametrize("key", list(synth.CONFIGS))
+def test_quantize_weights_parity(key):
+    need_gpu()
+    g = synth.generate(key, M=8, with_second_layer=False)
+    bits = g["cfg"].bits
+    for name, W in g["W"].items():
+        Wq, ws = rq.quantize_weights(dev_from_bits(W, "f32"), bits=bits)
+        torch.cuda.synchronize()
+        ref_c, ref_s, ref_p = oracle.quantize_rows(W, oracle.F32, bits, want_pre=True)
+        assert compare_codes(codes_np(Wq), ref_c, ref_p, bits, W.shape[1]) == 0, name
+        assert np.array_equal(ws.cpu().numpy().view(np.uint32), ref_s.view(np.uint32)), name
+
+
+GEMM_CASES = [(1, 16, 128, 8), (37, 48, 256, 8), (255, 272, 1024, 8), (257, 256, 384, 8),
+              (600, 1040, 1024, 8), (300, 512, 4096, 8), (129, 64, 6144, 8),
+              (1, 16, 256, 4), (200, 272, 1024, 4), (517, 1024, 4096, 4)]
+
+
+def _random_codes(rng, rows, K, bits):
+    q = 127 if bits == 8 else 7
+    c = rng.integers(-q, q + 1, (rows, K)).astype(np.int8)
+    c[rng.random(rows) < 0.05] = q           # a few all-q_max rows: extreme accumulators
+    return c
+
+
+@pytest.mark.parametrize("M,N,K,bits", GEMM_CASES)
+def test_gemm_s32_parity(M, N, K, bits):
+    need_gpu()
+    rng = np.random.default_rng(M * N + K)
+    A = _random_codes(rng, M, K, bits)
+    B = _random_codes(rng, N, K, bits)
+    Ad = torch.from_numpy(oracle.pack_codes(A, bits)).cuda()
+    Bd = torch.from_numpy(oracle.pack_codes(B, bits)).cuda()
+    acc = rq.gemm_s32(Ad, Bd, bits=bits, K=K)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), oracle.gemm_s32(A, B))
+
+
+@pytest.mark.parametrize("M,N,K,bits", GEMM_CASES[::2])
+@pytest.mark.parametrize("io", ["f16", "bf16"])
+@pytest.mark.parametrize("with_bias", [True, False])
+def test_gemm_dequant_parity(M, N, K, bits, io, with_bias):
+    need_gpu()
+    rng = np.random.default_rng(M + N + K + bits)
+    A = _random_codes(rng, M, K, bits)
+    B = _random_codes(rng, N, K, bits)
+    sx = (rng.random(M) * 0.05).astype(np.float32)
+    sw = (rng.random(N) * 2e-4).astype(np.float32)
+    b = rng.normal(0, 0.01, N).astype(np.float32) if with_bias else None
+    dev = lambda a: torch.from_numpy(a).cuda()
+    Y = rq.gemm_dequant(dev(oracle.pack_codes(A, bits)), dev(sx), dev(oracle.pack_codes(B, bits)),
+                        dev(sw), dev(b) if b is not None else None, bits=bits, K=K,
+                        out_dtype=torch.float16 if io == "f16" else torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = oracle.epilogue(oracle.gemm_s32(A, B), sx, sw, b, IO_CODE[io])
+    got = bits_from_dev(Y)
+    ok, maxerr = y_tolerance_ok(got, ref, io)
+    assert ok, maxerr
+    assert np.array_equal(got, ref)
+
+
+def _linear_case(xb, io, W, b, bits):
+    Wd = dev_from_bits(W, "f32")
+    Wq, ws = rq.quantize_weights(Wd, bits=bits)
+    Xd = dev_from_bits(xb, io)
+    bd = torch.from_numpy(b).cuda() if b is not None else None
+    Y = rq.rotq_linear(Xd, Wq, ws, bd, bits=bits)
+    torch.cuda.synchronize()
+    wc, _, wsr = oracle.quantize_weights(W, bits)
+    ref = oracle.rotq_linear(xb, IO_CODE[io], wc, wsr, b, bits)
+    return bits_from_dev(Y), ref["Y"], Wq, ws, wsr
+
+
+@pytest.mark.parametrize("key", list(synth.CONFIGS))
+@pytest.mark.parametrize("M", [1, 77, 333])
+def test_rotq_linear_parity_small(key, M):
+    need_gpu()
+    g = synth.generate(key, M=M)
+    cfg = g["cfg"]
+    for lin in cfg.linears:
+        xb = g["x_bits"] if lin.source == "x" else g["x2_bits"][lin.name]
+        got, ref, _, ws, wsr = _linear_case(xb, cfg.io, g["W"][lin.name], g["bias"][lin.name], cfg.bits)
+        assert np.array_equal(ws.cpu().numpy(), wsr)
+        ok, maxerr = y_tolerance_ok(got, ref, cfg.io)
+        assert ok, (lin.name, maxerr)
+        assert np.array_equal(got, ref), lin.name
+
+
+def test_rotq_linear_no_bias_and_zero_rows():
+    need_gpu()
+    rng = np.random.default_rng(5)
+    x = synth.random_rows(rng, 40, 512, "normal", 3, 50.0)
+    x[[0, 17, 39]] = 0
+    W = rng.normal(0, 0.02, (48, 512)).astype(np.float32)
+    W[5] = 0
+    b = rng.normal(0, 0.01, 48).astype(np.float32)
+    for bias in (b, None):
+        got, ref, *_ = _linear_case(synth.to_io_bits(x, "f16"), "f16", W, bias, 8)
+        assert np.array_equal(got, ref)
+    got, ref, *_ = _linear_case(synth.to_io_bits(x, "f16"), "f16", W, b, 8)
+    assert np.array_equal(got[17], b.astype(np.float16).view(np.uint16))   # zero X row -> bias
+
+
+def test_fp16_overflow_matches_oracle():
+    # Round-to-nearest-even with overflow to +-inf on the fp16 store.
+    need_gpu()
+    rng = np.random.default_rng(6)
+    x = synth.random_rows(rng, 8, 256, "normal", 0, 1.0)
+    W = rng.normal(0, 0.02, (32, 256)).astype(np.float32)
+    b = np.full(32, 65519.0, np.float32)
+    b[::2] = -70000.0
+    got, ref, *_ = _linear_case(synth.to_io_bits(x, "f16"), "f16", W, b, 8)
+    assert np.array_equal(got, ref)
+    assert np.isinf(got.view(np.float16)[:, ::2]).all()
+
+
+def test_deterministic_bits():
+    need_gpu()
+    g = synth.generate("dit", M=1000, with_second_layer=False)
+    W = dev_from_bits(g["W"]["qkv"], "f32")
+    Wq, ws = rq.quantize_weights(W)
+    X = dev_from_bits(g["x_bits"], "bf16")
+    y1 = rq.rotq_linear(X, Wq, ws)
+    y2 = rq.rotq_linear(X, Wq, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_runtime_errors_are_raised():
+    need_gpu()
+    X = torch.zeros(16, 1000, dtype=torch.float16, device="cuda")
+    with pytest.raises(rq.ConvRotError) as e:
+        rq.rotate_quantize(X)
+    assert e.value.status == rq.RQ_EUNSUPPORTED
+    Wq = torch.zeros(32, 128, dtype=torch.int8, device="cuda")
+    ws = torch.zeros(32, dtype=torch.float32, device="cuda")
+    X = torch.zeros(16, 128, dtype=torch.float16, device="cuda")
+    small = torch.empty(64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(rq.ConvRotError) as e:
+        rq.rotq_linear(X, Wq, ws, workspace=small)
+    assert e.value.status == rq.RQ_EWORKSPACE

@@ -1,0 +1,233 @@
+"""Thin ctypes binding over libconvrot.so (the C ABI in include/convrot.h).
+
+Argument marshalling only: every step of the quantized linear runs in the HIP kernels of the
+library. PyTorch supplies device memory and the current HIP stream. There is no fallback: if
+the library is missing or a call fails, a ConvRotError is raised.
+
+Two layers:
+  * ``rq_*`` -- the C entry points under their own names, taking integer device pointers;
+  * ``quantize_weights``, ``rotq_linear``, ``rotate_quantize``, ``gemm_dequant``,
+    ``gemm_s32`` -- tensor wrappers that allocate outputs with torch and pass the current
+    stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(PKG, "libconvrot.so")
+
+RQ_OK, RQ_EINVAL, RQ_EUNSUPPORTED, RQ_EWORKSPACE, RQ_EHIP = range(5)
+RQ_F32, RQ_F16, RQ_BF16 = 0, 1, 2
+RQ_ROT_WHT = 1
+
+
+class ConvRotError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__("%s failed: %s (%s)" % (where, _status_text(status), detail))
+
+
+class rq_qconfig(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_int32), ("rot_kind", ctypes.c_int32), ("rot_block", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libconvrot.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise FileNotFoundError(
+            "libconvrot.so is not built (%s); run __graft_entry__.build() or "
+            "python w4a4_integer_quantized_amd/build.py" % _LIB_PATH)
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    CFG = ctypes.POINTER(rq_qconfig)
+    sig = {
+        "rq_quantize_weights": [P, I32, I64, I64, CFG, P, P, P],
+        "rq_rotate_quantize": [P, I32, I64, I64, CFG, P, P, P],
+        "rq_rotq_linear": [P, I32, I64, I64, P, P, I64, P, CFG, P, P, SZ, P],
+        "rq_gemm_dequant": [P, P, P, P, P, I64, I64, I64, CFG, P, I32, P],
+        "rq_gemm_s32": [P, P, I64, I64, I64, CFG, P, P],
+        "rq_check_rotq_linear_args": [P, I32, I64, I64, P, P, I64, P, CFG, P, P, SZ],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    lib.rq_rotq_linear_workspace_size.argtypes = [I64, I64, CFG]
+    lib.rq_rotq_linear_workspace_size.restype = SZ
+    lib.rq_status_string.argtypes = [ctypes.c_int]
+    lib.rq_status_string.restype = ctypes.c_char_p
+    lib.rq_last_error_detail.argtypes = []
+    lib.rq_last_error_detail.restype = ctypes.c_char_p
+    lib.rq_version.argtypes = []
+    lib.rq_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _status_text(s: int) -> str:
+    try:
+        return load().rq_status_string(s).decode()
+    except Exception:  # pragma: no cover - only when the library itself is unusable
+        return "status %d" % s
+
+
+def _check(status: int, where: str):
+    if status != RQ_OK:
+        raise ConvRotError(status, where, load().rq_last_error_detail().decode())
+
+
+def make_cfg(bits: int = 8, rot_block: int = 128, rot_kind: int = RQ_ROT_WHT) -> rq_qconfig:
+    return rq_qconfig(bits, rot_kind, rot_block)
+
+
+# ----------------------------------------------------------------------------- raw entry points
+def rq_quantize_weights(W, w_dtype, N, K, cfg, Wq, w_scale, stream) -> int:
+    return load().rq_quantize_weights(W, w_dtype, N, K, ctypes.byref(cfg), Wq, w_scale, stream)
+
+
+def rq_rotate_quantize(X, x_dtype, M, K, cfg, Xq, x_scale, stream) -> int:
+    return load().rq_rotate_quantize(X, x_dtype, M, K, ctypes.byref(cfg), Xq, x_scale, stream)
+
+
+def rq_rotq_linear(X, x_dtype, M, K, Wq, w_scale, N, bias, cfg, Y, ws, ws_bytes, stream) -> int:
+    return load().rq_rotq_linear(X, x_dtype, M, K, Wq, w_scale, N, bias, ctypes.byref(cfg), Y, ws,
+                                 ws_bytes, stream)
+
+
+def rq_gemm_dequant(Xq, x_scale, Wq, w_scale, bias, M, N, K, cfg, Y, y_dtype, stream) -> int:
+    return load().rq_gemm_dequant(Xq, x_scale, Wq, w_scale, bias, M, N, K, ctypes.byref(cfg), Y,
+                                  y_dtype, stream)
+
+
+def rq_gemm_s32(Xq, Wq, M, N, K, cfg, acc, stream) -> int:
+    return load().rq_gemm_s32(Xq, Wq, M, N, K, ctypes.byref(cfg), acc, stream)
+
+
+def rq_rotq_linear_workspace_size(M, K, cfg) -> int:
+    return load().rq_rotq_linear_workspace_size(M, K, ctypes.byref(cfg))
+
+
+def rq_check_rotq_linear_args(X, x_dtype, M, K, Wq, w_scale, N, bias, cfg, Y, ws, ws_bytes) -> int:
+    return load().rq_check_rotq_linear_args(X, x_dtype, M, K, Wq, w_scale, N, bias,
+                                            ctypes.byref(cfg), Y, ws, ws_bytes)
+
+
+def rq_status_string(s: int) -> str:
+    return load().rq_status_string(s).decode()
+
+
+# ----------------------------------------------------------------------------- tensor wrappers
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return RQ_F32
+    if t.dtype == torch.float16:
+        return RQ_F16
+    if t.dtype == torch.bfloat16:
+        return RQ_BF16
+    raise TypeError("unsupported dtype %s" % t.dtype)
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t.data_ptr()
+
+
+def code_shape(rows: int, K: int, bits: int) -> Tuple[int, int]:
+    return (rows, K if bits == 8 else K // 2)
+
+
+def workspace_size(M: int, K: int, bits: int = 8) -> int:
+    return rq_rotq_linear_workspace_size(M, K, make_cfg(bits))
+
+
+def quantize_weights(W, bits: int = 8, rot: int = 128, stream=None):
+    """Offline: W [N, K] (f32/f16/bf16, device) -> (Wq int8 [N, K] | uint8 [N, K/2], w_scale f32 [N])."""
+    torch = _torch()
+    N, K = W.shape
+    Wq = torch.empty(code_shape(N, K, bits), dtype=torch.int8 if bits == 8 else torch.uint8, device=W.device)
+    ws = torch.empty((N,), dtype=torch.float32, device=W.device)
+    _check(rq_quantize_weights(_dev(W, "W"), _dtype_code(W), N, K, make_cfg(bits, rot),
+                               Wq.data_ptr(), ws.data_ptr(), _stream(stream)), "rq_quantize_weights")
+    return Wq, ws
+
+
+def rotate_quantize(X, bits: int = 8, rot: int = 128, stream=None):
+    """Online step alone: X [M, K] -> (Xq, x_scale f32 [M])."""
+    torch = _torch()
+    M, K = X.shape
+    Xq = torch.empty(code_shape(M, K, bits), dtype=torch.int8 if bits == 8 else torch.uint8, device=X.device)
+    xs = torch.empty((M,), dtype=torch.float32, device=X.device)
+    _check(rq_rotate_quantize(_dev(X, "X"), _dtype_code(X), M, K, make_cfg(bits, rot),
+                              Xq.data_ptr(), xs.data_ptr(), _stream(stream)), "rq_rotate_quantize")
+    return Xq, xs
+
+
+def rotq_linear(X, Wq, w_scale, bias=None, bits: int = 8, rot: int = 128, workspace=None,
+                out=None, stream=None):
+    """Y [M, N] = dequant(int GEMM(rotate+quantize(X), Wq)) + bias, in X's dtype."""
+    torch = _torch()
+    M, K = X.shape
+    N = Wq.shape[0]
+    cfg = make_cfg(bits, rot)
+    need = rq_rotq_linear_workspace_size(M, K, cfg)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=X.device)
+    Y = torch.empty((M, N), dtype=X.dtype, device=X.device) if out is None else out
+    _check(rq_rotq_linear(_dev(X, "X"), _dtype_code(X), M, K, _dev(Wq, "Wq"), _dev(w_scale, "w_scale"),
+                          N, _dev(bias, "bias") if bias is not None else None, cfg, _dev(Y, "Y"),
+                          _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                          _stream(stream)), "rq_rotq_linear")
+    return Y
+
+
+def gemm_dequant(Xq, x_scale, Wq, w_scale, bias=None, bits: int = 8, K: Optional[int] = None,
+                 out_dtype=None, stream=None):
+    torch = _torch()
+    M = Xq.shape[0]
+    N = Wq.shape[0]
+    K = K if K is not None else (Xq.shape[1] if bits == 8 else 2 * Xq.shape[1])
+    out_dtype = torch.float16 if out_dtype is None else out_dtype
+    Y = torch.empty((M, N), dtype=out_dtype, device=Xq.device)
+    _check(rq_gemm_dequant(_dev(Xq, "Xq"), _dev(x_scale, "x_scale"), _dev(Wq, "Wq"), _dev(w_scale, "w_scale"),
+                           _dev(bias, "bias") if bias is not None else None, M, N, K, make_cfg(bits),
+                           Y.data_ptr(), _dtype_code(Y), _stream(stream)), "rq_gemm_dequant")
+    return Y
+
+
+def gemm_s32(Xq, Wq, bits: int = 8, K: Optional[int] = None, stream=None):
+    torch = _torch()
+    M = Xq.shape[0]
+    N = Wq.shape[0]
+    K = K if K is not None else (Xq.shape[1] if bits == 8 else 2 * Xq.shape[1])
+    acc = torch.empty((M, N), dtype=torch.int32, device=Xq.device)
+    _check(rq_gemm_s32(_dev(Xq, "Xq"), _dev(Wq, "Wq"), M, N, K, make_cfg(bits), acc.data_ptr(),
+                       _stream(stream)), "rq_gemm_s32")
+    return acc

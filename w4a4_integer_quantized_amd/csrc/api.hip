@@ -1,0 +1,246 @@
+// api.hip -- the C ABI of libconvrot.so (declared and documented in include/convrot.h).
+//
+// Host side only: argument validation (a pure function of the arguments, no HIP call),
+// workspace carving, and the launches of the two kernels on the caller's stream. Nothing is
+// allocated and no state is kept between calls.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "convrot.h"
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_detail;
+
+constexpr int64_t kMaxK = 131072;          // int32 accumulators: 127^2 * K and 256 * 7^2 * K < 2^31
+constexpr int64_t kMaxRowsOrCols = (int64_t(1) << 31) - 1;
+
+rq_status fail(rq_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+rq_status fail(rq_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_detail = buf;
+  return s;
+}
+
+rq_status ok() { return RQ_OK; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t elem_size(int32_t dt) { return dt == RQ_F32 ? 4 : 2; }
+
+int64_t code_bytes(int64_t rows, int64_t K, int bits) { return bits == 8 ? rows * K : rows * K / 2; }
+
+int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
+
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+  if (!a || !b || na <= 0 || nb <= 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+rq_status check_cfg(const rq_qconfig* cfg) {
+  if (!cfg) return fail(RQ_EINVAL, "cfg is NULL");
+  if (cfg->bits != 8 && cfg->bits != 4)
+    return fail(RQ_EUNSUPPORTED, "bits = %d (supported: 8, 4)", cfg->bits);
+  if (cfg->rot_kind != RQ_ROT_WHT)
+    return fail(RQ_EUNSUPPORTED, "rot_kind = %d (supported: RQ_ROT_WHT)", cfg->rot_kind);
+  if (cfg->rot_block != 128)
+    return fail(RQ_EUNSUPPORTED, "rot_block = %d (supported: 128)", cfg->rot_block);
+  return ok();
+}
+
+rq_status check_rows_k(int64_t rows, int64_t K, const char* what) {
+  if (rows < 0) return fail(RQ_EINVAL, "%s rows = %lld < 0", what, (long long)rows);
+  if (rows > kMaxRowsOrCols) return fail(RQ_EUNSUPPORTED, "%s rows = %lld >= 2^31", what, (long long)rows);
+  if (K < 128 || K % 128 != 0 || K > kMaxK)
+    return fail(RQ_EUNSUPPORTED, "K = %lld (need a multiple of 128 in [128, %lld])", (long long)K,
+                (long long)kMaxK);
+  return ok();
+}
+
+rq_status check_gemm_shape(int64_t M, int64_t N, int64_t K, int bits) {
+  rq_status s = check_rows_k(M, K, "M");
+  if (s) return s;
+  if (N <= 0 || N % 16 != 0 || N > kMaxRowsOrCols)
+    return fail(RQ_EUNSUPPORTED, "N = %lld (need a positive multiple of 16 below 2^31)", (long long)N);
+  if (bits == 4 && K % 256 != 0)
+    return fail(RQ_EUNSUPPORTED, "4-bit GEMM needs K %% 256 == 0 (K = %lld)", (long long)K);
+  return ok();
+}
+
+rq_status check_ptr(const void* p, const char* name, bool required = true) {
+  if (!p) return required ? fail(RQ_EINVAL, "%s is NULL", name) : ok();
+  if (!aligned16(p)) return fail(RQ_EINVAL, "%s is not 16-byte aligned", name);
+  return ok();
+}
+
+rq_status from_hip(hipError_t e, const char* where) {
+  if (e == hipSuccess) return RQ_OK;
+  return fail(RQ_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+rq_status check_rotate_args(const void* X, int32_t dt, int64_t rows, int64_t K, const rq_qconfig* cfg,
+                            const void* Q, const float* S, const char* xname) {
+  rq_status s = check_cfg(cfg);
+  if (s) return s;
+  if (dt != RQ_F32 && dt != RQ_F16 && dt != RQ_BF16) return fail(RQ_EINVAL, "bad %s dtype %d", xname, dt);
+  if ((s = check_rows_k(rows, K, xname))) return s;
+  if (rows == 0) return ok();
+  if ((s = check_ptr(X, xname))) return s;
+  if ((s = check_ptr(Q, "codes output"))) return s;
+  if (!S) return fail(RQ_EINVAL, "scale output is NULL");
+  if ((reinterpret_cast<uintptr_t>(S) & 3u) != 0) return fail(RQ_EINVAL, "scale output is not 4-byte aligned");
+  const int64_t xb = rows * K * elem_size(dt), qb = code_bytes(rows, K, cfg->bits);
+  if (overlap(X, xb, Q, qb) || overlap(X, xb, S, rows * 4) || overlap(Q, qb, S, rows * 4))
+    return fail(RQ_EINVAL, "input, codes and scales must not overlap");
+  return ok();
+}
+
+rq_status check_linear(const void* X, int32_t x_dtype, int64_t M, int64_t K, const void* Wq,
+                       const float* w_scale, int64_t N, const float* bias, const rq_qconfig* cfg,
+                       const void* Y, const void* ws, size_t ws_bytes) {
+  rq_status s = check_cfg(cfg);
+  if (s) return s;
+  if (x_dtype != RQ_F16 && x_dtype != RQ_BF16)
+    return fail(x_dtype == RQ_F32 ? RQ_EUNSUPPORTED : RQ_EINVAL,
+                "X dtype %d (supported: RQ_F16, RQ_BF16; Y has X's dtype)", x_dtype);
+  if ((s = check_gemm_shape(M, N, K, cfg->bits))) return s;
+  if (M == 0) return ok();
+  if ((s = check_ptr(X, "X"))) return s;
+  if ((s = check_ptr(Wq, "Wq"))) return s;
+  if ((s = check_ptr(w_scale, "w_scale"))) return s;
+  if ((s = check_ptr(bias, "bias", false))) return s;
+  if ((s = check_ptr(Y, "Y"))) return s;
+  if ((s = check_ptr(ws, "workspace"))) return s;
+  const size_t need = rq_rotq_linear_workspace_size(M, K, cfg);
+  if (ws_bytes < need)
+    return fail(RQ_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  const int64_t xb = M * K * 2, wb = code_bytes(N, K, cfg->bits), yb = M * N * 2;
+  if (overlap(Y, yb, X, xb) || overlap(Y, yb, Wq, wb) || overlap(Y, yb, ws, (int64_t)need) ||
+      overlap(Y, yb, w_scale, N * 4) || overlap(Y, yb, bias, N * 4))
+    return fail(RQ_EINVAL, "Y overlaps an input or the workspace");
+  if (overlap(ws, (int64_t)need, X, xb) || overlap(ws, (int64_t)need, Wq, wb) ||
+      overlap(ws, (int64_t)need, w_scale, N * 4) || overlap(ws, (int64_t)need, bias, N * 4))
+    return fail(RQ_EINVAL, "workspace overlaps an input");
+  return ok();
+}
+
+rq_status check_gemm(const void* Xq, const float* x_scale, const void* Wq, const float* w_scale,
+                     const float* bias, int64_t M, int64_t N, int64_t K, const rq_qconfig* cfg,
+                     const void* out, int64_t out_elem) {
+  rq_status s = check_cfg(cfg);
+  if (s) return s;
+  if ((s = check_gemm_shape(M, N, K, cfg->bits))) return s;
+  if (M == 0) return ok();
+  if ((s = check_ptr(Xq, "Xq"))) return s;
+  if ((s = check_ptr(Wq, "Wq"))) return s;
+  if ((s = check_ptr(out, "output"))) return s;
+  if (x_scale && (reinterpret_cast<uintptr_t>(x_scale) & 3u)) return fail(RQ_EINVAL, "x_scale misaligned");
+  if ((s = check_ptr(w_scale, "w_scale", out_elem != 4))) return s;
+  if ((s = check_ptr(bias, "bias", false))) return s;
+  if (out_elem != 4 && !x_scale) return fail(RQ_EINVAL, "x_scale is NULL");
+  const int64_t ob = M * N * out_elem;
+  if (overlap(out, ob, Xq, code_bytes(M, K, cfg->bits)) || overlap(out, ob, Wq, code_bytes(N, K, cfg->bits)) ||
+      overlap(out, ob, x_scale, M * 4) || overlap(out, ob, w_scale, N * 4) || overlap(out, ob, bias, N * 4))
+    return fail(RQ_EINVAL, "output overlaps an input");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rq_status_string(rq_status s) {
+  switch (s) {
+    case RQ_OK: return "RQ_OK: success";
+    case RQ_EINVAL: return "RQ_EINVAL: invalid argument (NULL, misaligned, negative size, bad dtype, overlap)";
+    case RQ_EUNSUPPORTED: return "RQ_EUNSUPPORTED: shape or configuration outside the supported limits";
+    case RQ_EWORKSPACE: return "RQ_EWORKSPACE: workspace too small";
+    case RQ_EHIP: return "RQ_EHIP: HIP runtime error";
+  }
+  return "unknown rq_status";
+}
+
+const char* rq_last_error_detail(void) { return g_detail.c_str(); }
+
+const char* rq_version(void) { return "0.1.0"; }
+
+size_t rq_rotq_linear_workspace_size(int64_t M, int64_t K, const rq_qconfig* cfg) {
+  if (check_cfg(cfg) != RQ_OK || M < 0 || K <= 0) return 0;
+  return (size_t)(round256(code_bytes(M, K, cfg->bits)) + round256(M * 4));
+}
+
+rq_status rq_quantize_weights(const void* W, int32_t w_dtype, int64_t N, int64_t K,
+                              const rq_qconfig* cfg, void* Wq, float* w_scale, void* stream) {
+  rq_status s = check_rotate_args(W, w_dtype, N, K, cfg, Wq, w_scale, "W");
+  if (s) return s;
+  return from_hip(convrot::launch_rotate_quant(W, w_dtype, N, K, cfg->bits, Wq, w_scale,
+                                               static_cast<hipStream_t>(stream)),
+                  "rotate_quant launch");
+}
+
+rq_status rq_rotate_quantize(const void* X, int32_t x_dtype, int64_t M, int64_t K,
+                             const rq_qconfig* cfg, void* Xq, float* x_scale, void* stream) {
+  rq_status s = check_rotate_args(X, x_dtype, M, K, cfg, Xq, x_scale, "X");
+  if (s) return s;
+  return from_hip(convrot::launch_rotate_quant(X, x_dtype, M, K, cfg->bits, Xq, x_scale,
+                                               static_cast<hipStream_t>(stream)),
+                  "rotate_quant launch");
+}
+
+rq_status rq_check_rotq_linear_args(const void* X, int32_t x_dtype, int64_t M, int64_t K,
+                                    const void* Wq, const float* w_scale, int64_t N,
+                                    const float* bias, const rq_qconfig* cfg, const void* Y,
+                                    const void* workspace, size_t ws_bytes) {
+  return check_linear(X, x_dtype, M, K, Wq, w_scale, N, bias, cfg, Y, workspace, ws_bytes);
+}
+
+rq_status rq_rotq_linear(const void* X, int32_t x_dtype, int64_t M, int64_t K, const void* Wq,
+                         const float* w_scale, int64_t N, const float* bias,
+                         const rq_qconfig* cfg, void* Y, void* workspace, size_t ws_bytes,
+                         void* stream) {
+  rq_status s = check_linear(X, x_dtype, M, K, Wq, w_scale, N, bias, cfg, Y, workspace, ws_bytes);
+  if (s || M == 0) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* Xq = static_cast<uint8_t*>(workspace);
+  float* sx = reinterpret_cast<float*>(Xq + round256(code_bytes(M, K, cfg->bits)));
+  if ((s = from_hip(convrot::launch_rotate_quant(X, x_dtype, M, K, cfg->bits, Xq, sx, st),
+                    "rotate_quant launch")))
+    return s;
+  return from_hip(convrot::launch_gemm(Xq, sx, Wq, w_scale, bias, M, N, K, cfg->bits, Y,
+                                       x_dtype, nullptr, st),
+                  "gemm launch");
+}
+
+rq_status rq_gemm_dequant(const void* Xq, const float* x_scale, const void* Wq,
+                          const float* w_scale, const float* bias, int64_t M, int64_t N,
+                          int64_t K, const rq_qconfig* cfg, void* Y, int32_t y_dtype,
+                          void* stream) {
+  if (y_dtype != RQ_F16 && y_dtype != RQ_BF16)
+    return fail(y_dtype == RQ_F32 ? RQ_EUNSUPPORTED : RQ_EINVAL, "Y dtype %d (supported: RQ_F16, RQ_BF16)", y_dtype);
+  rq_status s = check_gemm(Xq, x_scale, Wq, w_scale, bias, M, N, K, cfg, Y, 2);
+  if (s || M == 0) return s;
+  return from_hip(convrot::launch_gemm(Xq, x_scale, Wq, w_scale, bias, M, N, K, cfg->bits, Y,
+                                       y_dtype, nullptr, static_cast<hipStream_t>(stream)),
+                  "gemm launch");
+}
+
+rq_status rq_gemm_s32(const void* Xq, const void* Wq, int64_t M, int64_t N, int64_t K,
+                      const rq_qconfig* cfg, int32_t* acc, void* stream) {
+  rq_status s = check_gemm(Xq, nullptr, Wq, nullptr, nullptr, M, N, K, cfg, acc, 4);
+  if (s || M == 0) return s;
+  return from_hip(convrot::launch_gemm(Xq, nullptr, Wq, nullptr, nullptr, M, N, K, cfg->bits,
+                                       acc, RQ_F16, acc, static_cast<hipStream_t>(stream)),
+                  "gemm launch");
+}
+
+}  // extern "C"
