@@ -1,0 +1,257 @@
+"""Benchmark of the ConvRot quantized linear on one MI355X.
+
+One step = one pass of the hot path over one batch: for every linear of the workload,
+rotate + quantize the activations (HIP kernel 1), int8 MFMA GEMM with the fused dequantizing
+epilogue (HIP kernel 2). The default workload is ViT-L attention projections at batch 8:
+X f16 [41472, 1024] through qkv (N = 3072) and out-proj (N = 1024), both W8A8; weights are
+quantized once, offline, before timing (reported separately).
+
+Prints ONE JSON line. `value` = whole-step throughput in TOPS (2*M*N*K summed over the calls,
+divided by the wall time of the timed steps, inputs already resident in HBM). A ring of input /
+output buffer sets larger than the 256 MB Infinity Cache is rotated so that no step reads what
+the previous one left in the cache. Per-kernel durations come from HIP events recorded on the
+launch stream between the kernels of the same hot path (split into its two calls); they feed the
+`roofline` object of the dominant kernel (the GEMM of the largest call) and the per-call
+breakdown. `cpu_baseline` times the CPU oracle (never tuned) on a bounded row sample of the
+same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, TOP/s
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
+MALL_BYTES = 256 << 20
+PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+
+
+def log(msg):
+    sys.stderr.write("[bench] %s\n" % msg)
+    sys.stderr.flush()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("gemm_i8.hip", "rotate_quant.hip"):
+        with open(os.path.join(ROOT, "w4a4_integer_quantized_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_counters(workload, kernel):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE runs (scaled by a
+    copy-kernel calibration), or None if absent or taken on different kernel sources."""
+    try:
+        with open(PMC_FILE) as fh:
+            d = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("workloads", {}).get(workload, {}).get(kernel)
+
+
+def cpu_baseline(g, cfg, target_s):
+    """The CPU oracle as it stands on a bounded sample of the same workload's rows."""
+    import numpy as np
+    import oracle
+    dt = oracle.F16 if cfg.io == "f16" else oracle.BF16
+    wq = {lin.name: oracle.quantize_weights(g["W"][lin.name], cfg.bits)[0::2] for lin in cfg.linears}
+
+    def run(rows):
+        t0 = time.perf_counter()
+        ops = 0
+        for lin in cfg.linears:
+            src = g["x_bits"] if lin.source == "x" else g["x2_bits"][lin.name]
+            wc, ws = wq[lin.name]
+            oracle.rotq_linear(np.ascontiguousarray(src[:rows]), dt, wc, ws, g["bias"][lin.name], cfg.bits)
+            ops += 2 * rows * lin.N * lin.K
+        return time.perf_counter() - t0, ops
+
+    t, _ = run(16)
+    rows = int(min(cfg.M, max(16, 16 * target_s / max(t, 1e-6))))
+    t, ops = run(rows)
+    return {"value": ops / t / 1e12, "unit": "TOPS", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "first %d of %d tokens, every linear of the step (rotate+quantize, int GEMM, "
+                      "epilogue); %.1f s" % (rows, cfg.M, t)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="vit_attn")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the quantized linear "
+              "shards over tokens with no exchange; see the design notes). Run with --gpus 1.")
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import w4a4_integer_quantized_amd as rq
+    from w4a4_integer_quantized_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cfg = synth.CONFIGS[args.workload]
+    log("generating %s" % cfg.workload)
+    g = synth.generate(args.workload)
+    tdt = torch.float16 if cfg.io == "f16" else torch.bfloat16
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    bits, M = cfg.bits, cfg.M
+
+    # Offline weight quantization (timed once, reported separately).
+    Wq, Ws, B = {}, {}, {}
+    wq_ms = 0.0
+    for lin in cfg.linears:
+        Wd = torch.from_numpy(g["W"][lin.name]).to(dev)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        Wq[lin.name], Ws[lin.name] = rq.quantize_weights(Wd, bits=bits)
+        torch.cuda.synchronize()
+        wq_ms += (time.perf_counter() - t0) * 1e3
+        B[lin.name] = torch.from_numpy(g["bias"][lin.name]).to(dev)
+        del Wd
+
+    # Ring of buffer sets (X copies, outputs, workspace) larger than the Infinity Cache.
+    x_host = torch.from_numpy(g["x_bits"].view(np.int16)).view(tdt)
+    set_bytes = x_host.numel() * 2
+    for lin in cfg.linears:
+        set_bytes += M * lin.N * 2 + rq.workspace_size(M, lin.K, bits)
+    R = max(2, min(8, math.ceil(3 * MALL_BYTES / set_bytes)))
+    sets = []
+    for _ in range(R):
+        s = {"X": x_host.to(dev), "Y": {}, "ws": {}}
+        for lin in cfg.linears:
+            s["Y"][lin.name] = torch.empty((M, lin.N), dtype=tdt, device=dev)
+            s["ws"][lin.name] = torch.empty((rq.workspace_size(M, lin.K, bits),), dtype=torch.uint8, device=dev)
+        sets.append(s)
+    log("ring of %d buffer sets, %.0f MB each" % (R, set_bytes / 1e6))
+    cfgc = rq.make_cfg(bits)
+    xdt = rq.RQ_F16 if cfg.io == "f16" else rq.RQ_BF16
+    sptr = stream.cuda_stream
+
+    def lin_input(s, lin):
+        if lin.source == "x":
+            return s["X"]
+        # MLP pair: the second layer's input is GELU of the first layer's output (torch op on the
+        # GPU, outside the library)
+        first = cfg.linears[0].name
+        approx = "tanh" if lin.source == "gelu_tanh" else "none"
+        return torch.nn.functional.gelu(s["Y"][first], approximate=approx)
+
+    def step(i):
+        s = sets[i % R]
+        for lin in cfg.linears:
+            X = lin_input(s, lin)
+            ws = s["ws"][lin.name]
+            st = rq.rq_rotq_linear(X.data_ptr(), xdt, M, lin.K, Wq[lin.name].data_ptr(),
+                                   Ws[lin.name].data_ptr(), lin.N, B[lin.name].data_ptr(), cfgc,
+                                   s["Y"][lin.name].data_ptr(), ws.data_ptr(), ws.numel(), sptr)
+            if st != rq.RQ_OK:
+                raise rq.ConvRotError(st, "rq_rotq_linear", rq.load().rq_last_error_detail().decode())
+
+    ops_per_step = sum(2 * M * lin.N * lin.K for lin in cfg.linears)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log("warmup done (%d steps)" % args.warmup)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    tops = ops_per_step * args.steps / wall / 1e12
+    log("timed %d steps: %.3f ms/step, %.1f TOPS" % (args.steps, ms_per_step, tops))
+
+    # Per-kernel durations: the same two kernels per call (rotate+quantize, GEMM+epilogue)
+    # launched through the split entry points, with HIP events between them on the stream.
+    nl = len(cfg.linears)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3 * nl)] for _ in range(args.steps)]
+
+    def split_step(i, evs):
+        s = sets[i % R]
+        for c, lin in enumerate(cfg.linears):
+            X = lin_input(s, lin)
+            xq = s["ws"][lin.name].data_ptr()                        # workspace = [Xq | x_scale]
+            xs = xq + (M * lin.K * bits // 8 + 255) // 256 * 256
+            evs[3 * c].record(stream)
+            st = rq.rq_rotate_quantize(X.data_ptr(), xdt, M, lin.K, cfgc, xq, xs, sptr)
+            evs[3 * c + 1].record(stream)
+            st |= rq.rq_gemm_dequant(xq, xs, Wq[lin.name].data_ptr(), Ws[lin.name].data_ptr(),
+                                     B[lin.name].data_ptr(), M, lin.N, lin.K, cfgc,
+                                     s["Y"][lin.name].data_ptr(), xdt, sptr)
+            evs[3 * c + 2].record(stream)
+            assert st == rq.RQ_OK
+
+    for i in range(min(args.warmup, 3)):
+        split_step(i, ev[0])
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        split_step(i, ev[i])
+    torch.cuda.synchronize()
+    calls = {}
+    for c, lin in enumerate(cfg.linears):
+        rq_ms = sum(ev[i][3 * c].elapsed_time(ev[i][3 * c + 1]) for i in range(args.steps)) / args.steps
+        gm_ms = sum(ev[i][3 * c + 1].elapsed_time(ev[i][3 * c + 2]) for i in range(args.steps)) / args.steps
+        ops = 2 * M * lin.N * lin.K
+        rq_bytes = M * lin.K * 2 + M * lin.K * bits // 8 + 4 * M
+        gemm_bytes = M * lin.K * bits // 8 + lin.N * lin.K * bits // 8 + 8 * lin.N + 4 * M + M * lin.N * 2
+        calls[lin.name] = {
+            "M": M, "N": lin.N, "K": lin.K,
+            "rotate_quant_us": round(rq_ms * 1e3, 2),
+            "rotate_quant_GBps": round(rq_bytes / (rq_ms * 1e-3) / 1e9, 1),
+            "rotate_quant_hbm_frac": round(rq_bytes / (rq_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "gemm_us": round(gm_ms * 1e3, 2),
+            "gemm_TOPS": round(ops / (gm_ms * 1e-3) / 1e12, 1),
+            "gemm_mfma_frac": round(ops / (gm_ms * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+            "call_TOPS": round(ops / ((rq_ms + gm_ms) * 1e-3) / 1e12, 1),
+            "call_int8_peak_frac": round(ops / ((rq_ms + gm_ms) * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+            "rotate_quant_alg_bytes": rq_bytes, "gemm_alg_bytes": gemm_bytes, "gemm_alg_ops": ops,
+        }
+    dom = max(cfg.linears, key=lambda l: l.N * l.K)
+    dc = calls[dom.name]
+    traffic = traffic_from_counters(args.workload, "gemm_" + dom.name)
+    roofline = {"bound": "mfma", "kernel": "gemm_kernel (%s: %dx%dx%d, W%dA%d)" % (dom.name, M, dom.N, dom.K, bits, bits),
+                "achieved": dc["gemm_TOPS"], "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
+                "frac": dc["gemm_mfma_frac"], "traffic": traffic,
+                "avg_launch_us": dc["gemm_us"], "alg_ops_per_launch": dc["gemm_alg_ops"]}
+    rq_traffic = traffic_from_counters(args.workload, "rotate_quant_" + dom.name)
+    roofline_rq = {"bound": "hbm", "kernel": "rotate_quant_kernel (%s input %dx%d)" % (dom.name, M, dom.K),
+                   "achieved": dc["rotate_quant_GBps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                   "frac": dc["rotate_quant_hbm_frac"], "traffic": rq_traffic,
+                   "avg_launch_us": dc["rotate_quant_us"], "alg_bytes_per_launch": dc["rotate_quant_alg_bytes"]}
+
+    out = {
+        "metric": "rotq_linear TOPS (rotate+quant+GEMM) and % of MI355X INT8 MFMA peak",
+        "value": round(tops, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": cfg.workload, "M": M, "K": cfg.K, "N": [l.N for l in cfg.linears],
+                   "io": cfg.io, "bits": bits, "calls_per_step": nl},
+        "int8_peak_frac": round(tops / PEAK_INT8_TOPS, 4),
+        "roofline": roofline, "roofline_rotate_quant": roofline_rq, "calls": calls,
+        "weight_quant_ms_offline": round(wq_ms, 3), "buffer_sets": R,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle, ~%.0f s)" % args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(g, cfg, args.cpu_seconds)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -7,15 +7,22 @@
 // the INT8 matrix cores, the fallback the same page describes ("Downloads"); gfx950 has no
 // int4 MFMA.
 //
-// Design (gfx950, 256 CUs in 8 XCDs, 160 KB LDS per CU, 64-wide waves):
-//   * 256 x 256 output tile per 256-thread workgroup, 4 waves in 2 x 2, each wave 128 x 128
-//     = 4 x 4 blocks of v_mfma_i32_32x32x32_i8 (256 int32 accumulators per lane).
-//   * K is staged 128 bytes per step (128 int8 codes or 256 int4 codes) for both operands,
-//     double-buffered in LDS (2 x 64 KB), filled with direct global->LDS 16-byte loads. Rows
-//     are 128 B; the 16-byte chunk c of row r is stored at position c ^ swz(r) so the MFMA
-//     fragment reads (ds_read_b128, 32 rows x 2 chunks per wave) are bank-conflict free.
+// Design (gfx950: 256 CUs in 8 XCDs, 160 KB LDS per CU, 64-wide waves, 512 VGPR+AGPR/SIMD):
+//   * A 256-thread workgroup owns a 256 (tokens) x 128 (outputs) tile; its 4 waves each own
+//     64 x 128 = 2 x 4 blocks of v_mfma_i32_32x32x32_i8 (128 int32 accumulators per lane).
+//     Registers (<= 256 per lane) and LDS (74 KB) are sized so that TWO workgroups share a CU:
+//     while one is in its epilogue, prologue or at a barrier, the other keeps the matrix cores
+//     busy.
+//   * K is staged 64 bytes per step (64 int8 or 128 int4 codes) through a 3-deep LDS ring
+//     filled by direct global->LDS 16-byte loads (prefetch distance 2 steps). Rows are 64 B;
+//     the 16-byte chunk c of row r sits at c ^ swz(r), which keeps the MFMA fragment reads
+//     (ds_read_b128, 32 rows x 2 chunks per wave) free of bank conflicts for 32- and 64-bank
+//     layouts alike.
 //   * The MFMA "A" operand is a Wq row block and "B" an Xq row block, so each lane ends with
-//     4 consecutive output columns of one token: 8-byte fp16/bf16 stores.
+//     4 consecutive output columns of one token. The epilogue converts them and parks the
+//     wave's 64 x 128 output block in LDS (16-byte chunks XOR-swizzled by row), then writes it
+//     back as full 256-byte row segments with 16-byte stores. w_scale, bias and x_scale for the
+//     tile are loaded at kernel start (latency hidden behind the mainloop) and read from LDS.
 //   * INT4: a 16-byte chunk of packed codes (32 nibbles) becomes two MFMA operands,
 //     (w << 4) & 0xF0F0F0F0 (even k) and w & 0xF0F0F0F0 (odd k): each byte is 16 * code,
 //     exact for codes in [-8, 7]. Both operands get the same k permutation, so the sum is
@@ -26,6 +33,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "internal.h"
 
 namespace convrot {
@@ -34,25 +43,32 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 256;        // tokens per tile
-constexpr int kBN = 256;        // output features per tile
-constexpr int kBKB = 128;       // K bytes per stage
+constexpr int kBM = 256;                       // tokens per tile
+constexpr int kBN = 128;                       // output features per tile
+constexpr int kBKB = 64;                       // K bytes per step
+constexpr int kStages = 3;
 constexpr int kThreads = 256;
-constexpr int kStageBytes = (kBM + kBN) * kBKB;   // 64 KB
+constexpr int kTileX = kBM * kBKB;             // 16 KB
+constexpr int kStageBytes = (kBM + kBN) * kBKB;   // 24 KB
+constexpr int kScaleOff = kStages * kStageBytes;  // 72 KB
+constexpr int kLdsBytes = kScaleOff + (2 * kBN + kBM) * 4;
+constexpr int kLoadsPerStep = kStageBytes / 1024 / 4;   // wave-wide 1 KB copies per wave: 6
 
 enum OutKind { kOutS32 = 0, kOutF16 = 1, kOutBF16 = 2 };
 
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// One wave copies 8 rows x 128 B (1 KB) from global memory into LDS rows [row0, row0 + 8).
-// Lane l fills LDS position (row0 + l/8, chunk l%8), which holds global chunk (l%8) ^ swz(row).
+// One wave copies 16 rows x 64 B (1 KB) of a K-contiguous operand into LDS rows
+// [row0, row0 + 16) of a tile. Lane l fills LDS position (row0 + l/4, chunk l%4), which holds
+// global chunk (l%4) ^ swz(row). Rows past the end of the operand re-read its last row (their
+// results are never stored).
 __device__ __forceinline__ void copy_rows(const uint8_t* __restrict__ g, int64_t ld, int row0,
                                           int grow0, int gmax, int k0, uint8_t* lds_tile,
                                           int lane) {
-  const int r = row0 + (lane >> 3);
-  const int c = (lane & 7) ^ swz(r);
+  const int r = row0 + (lane >> 2);
+  const int c = (lane & 3) ^ swz(r);
   int gr = grow0 + r;
   gr = gr < gmax ? gr : gmax - 1;
   const uint8_t* src = g + (int64_t)gr * ld + k0 + 16 * c;
@@ -63,22 +79,30 @@ __device__ __forceinline__ v4i read_frag(const uint8_t* lds_tile, int row, int c
   return *reinterpret_cast<const v4i*>(lds_tile + row * kBKB + ((chunk ^ swz(row)) << 4));
 }
 
-__device__ __forceinline__ uint16_t f32_to_f16_rne(float v) {
-  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
-}
-
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
   uint32_t u = __float_as_uint(v);
   u += 0x7FFFu + ((u >> 16) & 1u);
   return static_cast<uint16_t>(u >> 16);
 }
 
+// The epilogue rounds twice by definition: fma -> binary32, then binary32 -> fp16/bf16. The
+// empty asm pins each value as a binary32 register so the compiler cannot fuse the conversion
+// into the fma (v_fma_mix* rounds once, straight to fp16, which differs on rare ties).
+__device__ __forceinline__ uint32_t pack2(float a, float b, int out) {
+  asm volatile("" : "+v"(a), "+v"(b));
+  if (out == kOutF16) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<_Float16>(a)) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, static_cast<_Float16>(b)) << 16);
+  }
+  return (uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16);
+}
+
 template <int BITS, int OUT>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
+__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
     const uint8_t* __restrict__ Xq, const float* __restrict__ sx, const uint8_t* __restrict__ Wq,
     const float* __restrict__ sw, const float* __restrict__ bias, void* __restrict__ Y, int M,
     int N, int Kb, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
 
   const int ntiles = tiles_m * tiles_n;
   const int per_xcd = (ntiles + 7) >> 3;
@@ -90,118 +114,219 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
 
-  v16i acc[4][4];
+  // Per-tile epilogue operands, fetched now so their latency hides behind the mainloop.
+  float my_sw = 0.0f, my_b = 0.0f, my_sx = 0.0f;
+  if constexpr (OUT != kOutS32) {
+    const int n = n0 + (int)threadIdx.x, m = m0 + (int)threadIdx.x;
+    if (threadIdx.x < kBN && n < N) {
+      my_sw = sw[n];
+      my_b = bias ? bias[n] : 0.0f;
+    }
+    if (m < M) my_sx = sx[m];
+  }
+
+  v16i acc[4][2];
 #pragma unroll
   for (int a = 0; a < 4; a++)
 #pragma unroll
-    for (int b = 0; b < 4; b++)
+    for (int b = 0; b < 2; b++)
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[a][b][r] = 0;
 
+  // Stage s holds the Xq tile (256 rows) then the Wq tile (128 rows), 64 B per row.
   auto issue = [&](int stage, int k0) {
     uint8_t* tX = lds + stage * kStageBytes;
-    uint8_t* tW = tX + kBM * kBKB;
+    uint8_t* tW = tX + kTileX;
 #pragma unroll
-    for (int i = 0; i < 8; i++) copy_rows(Xq, Kb, (wave * 8 + i) * 8, m0, M, k0, tX, lane);
+    for (int i = 0; i < 4; i++) copy_rows(Xq, Kb, (wave * 4 + i) * 16, m0, M, k0, tX, lane);
 #pragma unroll
-    for (int i = 0; i < 8; i++) copy_rows(Wq, Kb, (wave * 8 + i) * 8, n0, N, k0, tW, lane);
+    for (int i = 0; i < 2; i++) copy_rows(Wq, Kb, (wave * 2 + i) * 16, n0, N, k0, tW, lane);
   };
 
-  auto compute = [&](int stage) {
+  // Fragments of one 32-byte k slice: 4 Wq row blocks and this wave's 2 Xq row blocks.
+  const int rsub = lane & 31, fhalf = lane >> 5;
+  auto read_frags = [&](int stage, int ks, v4i (&wf)[4], v4i (&xf)[2]) {
     const uint8_t* tX = lds + stage * kStageBytes;
-    const uint8_t* tW = tX + kBM * kBKB;
-    const int rsub = lane & 31, half = lane >> 5;
+    const uint8_t* tW = tX + kTileX;
+    const int chunk = 2 * ks + fhalf;
 #pragma unroll
-    for (int ks = 0; ks < 4; ks++) {
-      const int chunk = 2 * ks + half;
-      v4i wf[4], xf[4];
+    for (int a = 0; a < 4; a++) wf[a] = read_frag(tW, a * 32 + rsub, chunk);
 #pragma unroll
-      for (int a = 0; a < 4; a++) wf[a] = read_frag(tW, wn * 128 + a * 32 + rsub, chunk);
+    for (int b = 0; b < 2; b++) xf[b] = read_frag(tX, wave * 64 + b * 32 + rsub, chunk);
+  };
+  auto mfma_slice = [&](const v4i (&wf)[4], const v4i (&xf)[2]) {
+    if constexpr (BITS == 8) {
 #pragma unroll
-      for (int b = 0; b < 4; b++) xf[b] = read_frag(tX, wm * 128 + b * 32 + rsub, chunk);
-      if constexpr (BITS == 8) {
+      for (int a = 0; a < 4; a++)
 #pragma unroll
-        for (int a = 0; a < 4; a++)
+        for (int b = 0; b < 2; b++)
+          acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[a], xf[b], acc[a][b], 0, 0, 0);
+    } else {
+      v4i wlo[4], whi[4], xlo[2], xhi[2];
 #pragma unroll
-          for (int b = 0; b < 4; b++)
-            acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[a], xf[b], acc[a][b], 0, 0, 0);
-      } else {
-        v4i wlo[4], whi[4], xlo[4], xhi[4];
+      for (int a = 0; a < 4; a++)
 #pragma unroll
-        for (int a = 0; a < 4; a++)
+        for (int e = 0; e < 4; e++) {
+          wlo[a][e] = (wf[a][e] << 4) & 0xF0F0F0F0;
+          whi[a][e] = wf[a][e] & 0xF0F0F0F0;
+        }
 #pragma unroll
-          for (int e = 0; e < 4; e++) {
-            wlo[a][e] = (wf[a][e] << 4) & 0xF0F0F0F0;
-            whi[a][e] = wf[a][e] & 0xF0F0F0F0;
-          }
+      for (int b = 0; b < 2; b++)
 #pragma unroll
-        for (int b = 0; b < 4; b++)
+        for (int e = 0; e < 4; e++) {
+          xlo[b][e] = (xf[b][e] << 4) & 0xF0F0F0F0;
+          xhi[b][e] = xf[b][e] & 0xF0F0F0F0;
+        }
 #pragma unroll
-          for (int e = 0; e < 4; e++) {
-            xlo[b][e] = (xf[b][e] << 4) & 0xF0F0F0F0;
-            xhi[b][e] = xf[b][e] & 0xF0F0F0F0;
-          }
+      for (int a = 0; a < 4; a++)
 #pragma unroll
-        for (int a = 0; a < 4; a++)
-#pragma unroll
-          for (int b = 0; b < 4; b++) {
-            acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wlo[a], xlo[b], acc[a][b], 0, 0, 0);
-            acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(whi[a], xhi[b], acc[a][b], 0, 0, 0);
-          }
-      }
+        for (int b = 0; b < 2; b++) {
+          acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wlo[a], xlo[b], acc[a][b], 0, 0, 0);
+          acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(whi[a], xhi[b], acc[a][b], 0, 0, 0);
+        }
     }
   };
 
+  // One 64-byte k step from LDS stage `cur`: all 12 fragment reads first (those of slice 1
+  // interleaved with the MFMAs of slice 0), then -- when LOAD -- the 6 direct-to-LDS loads of
+  // the step two ahead, one after each MFMA. LOAD is a compile-time tag so that the whole step
+  // stays one scheduling region.
+  constexpr int kMfmaPerStep = BITS == 8 ? 16 : 32;
+  auto kstep = [&](auto load_tag, int cur, int load_stage, int load_k0) {
+    constexpr bool LOAD = decltype(load_tag)::value;
+    v4i wf[2][4], xf[2][2];
+    read_frags(cur, 0, wf[0], xf[0]);
+    read_frags(cur, 1, wf[1], xf[1]);
+    if constexpr (LOAD) issue(load_stage, load_k0);
+    mfma_slice(wf[0], xf[0]);
+    mfma_slice(wf[1], xf[1]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);          // slice 0 fragments
+#pragma unroll
+    for (int i = 0; i < 6; i++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // DS read (slice 1)
+    }
+    if constexpr (LOAD) {
+#pragma unroll
+      for (int i = 0; i < kLoadsPerStep; i++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // VMEM (global -> LDS)
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerStep - 6 - kLoadsPerStep, 0);
+    } else {
+      __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerStep - 6, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Workgroup barrier without the memory fence of __syncthreads (which would wait for every
+  // outstanding load, draining the prefetch ring); LDS visibility of the direct loads is
+  // established by each wave's own vmcnt wait before it.
+  auto step_barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Ring of 3 stages: step kt lives in stage kt % 3. At the top of step kt (when kt + 1 < nk)
+  // the loads of steps kt and kt+1 are in flight, 6 per wave each, so waiting until 6 remain
+  // lands step kt; the stage refilled during step kt (step kt+2's) was last read in step kt-1,
+  // which every wave finished before this step's barrier.
   const int nk = Kb / kBKB;
   issue(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  for (int kt = 0; kt < nk; kt++) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) issue(cur ^ 1, (kt + 1) * kBKB);
-    compute(cur);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+  if (nk > 1) issue(1, kBKB);
+  int kt = 0;
+  for (; kt + 2 < nk; kt++) {
+    asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    step_barrier();
+    kstep(std::true_type{}, kt % kStages, (kt + 2) % kStages, (kt + 2) * kBKB);
   }
+  for (; kt < nk; kt++) {
+    if (kt + 1 < nk) {
+      asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    step_barrier();
+    kstep(std::false_type{}, kt % kStages, 0, 0);
+  }
+  __syncthreads();
 
   // Epilogue. Lane l of block (a, b) holds D[n][m] for m = b*32 + l%32 and
-  // n = a*32 + 8*(r/4) + 4*(l/32) + r%4, r = 0..15.
-  const int msub = lane & 31, nq = 4 * (lane >> 5);
+  // n = a*32 + 8*(r/4) + 4*(l/32) + r%4, r = 0..15 (wave-local indices; the wave's tokens are
+  // rows wave*64 .. wave*64+63 of the tile).
+  const int msub = lane & 31, half = lane >> 5;
+  if constexpr (OUT == kOutS32) {
 #pragma unroll
-  for (int b = 0; b < 4; b++) {
-    const int m = m0 + wm * 128 + b * 32 + msub;
-    if (m >= M) continue;
-    const float xs = (OUT == kOutS32) ? 0.0f : sx[m];
+    for (int b = 0; b < 2; b++) {
+      const int m = m0 + wave * 64 + b * 32 + msub;
+      if (m >= M) continue;
+#pragma unroll
+      for (int a = 0; a < 4; a++)
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+          const int n = n0 + a * 32 + 8 * g + 4 * half;
+          if (n >= N) continue;
+          int v[4];
+#pragma unroll
+          for (int e = 0; e < 4; e++) v[e] = (BITS == 4) ? (acc[a][b][4 * g + e] >> 8) : acc[a][b][4 * g + e];
+          *reinterpret_cast<int4*>(static_cast<int32_t*>(Y) + (int64_t)m * N + n) = make_int4(v[0], v[1], v[2], v[3]);
+        }
+    }
+  } else {
+    // All of LDS is free now.
+    float* e_sw = reinterpret_cast<float*>(lds + kScaleOff);
+    float* e_b = e_sw + kBN;
+    float* e_sx = e_b + kBN;
+    if (threadIdx.x < kBN) {
+      e_sw[threadIdx.x] = my_sw;
+      e_b[threadIdx.x] = my_b;
+    }
+    e_sx[threadIdx.x] = my_sx;
+    __syncthreads();
+    uint8_t* stage = lds + wave * (64 * 256);     // this wave's 64 x 128 fp16 block
+    float xs[2];
+#pragma unroll
+    for (int b = 0; b < 2; b++) xs[b] = e_sx[wave * 64 + b * 32 + msub];
 #pragma unroll
     for (int a = 0; a < 4; a++) {
 #pragma unroll
       for (int g = 0; g < 4; g++) {
-        const int n = n0 + wn * 128 + a * 32 + 8 * g + nq;
-        if (n >= N) continue;
-        int v[4];
+        const int col = a * 32 + 8 * g + 4 * half;   // tile-local output column
+        const float4 s4 = *reinterpret_cast<const float4*>(e_sw + col);
+        const float4 b4 = *reinterpret_cast<const float4*>(e_b + col);
+        const float ws[4] = {s4.x, s4.y, s4.z, s4.w};
+        const float bs[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-        for (int e = 0; e < 4; e++) v[e] = (BITS == 4) ? (acc[a][b][4 * g + e] >> 8) : acc[a][b][4 * g + e];
-        if constexpr (OUT == kOutS32) {
-          int4 o = make_int4(v[0], v[1], v[2], v[3]);
-          *reinterpret_cast<int4*>(static_cast<int32_t*>(Y) + (int64_t)m * N + n) = o;
-        } else {
-          const float4 s4 = *reinterpret_cast<const float4*>(sw + n);
-          const float4 b4 = bias ? *reinterpret_cast<const float4*>(bias + n) : make_float4(0.f, 0.f, 0.f, 0.f);
-          const float ws[4] = {s4.x, s4.y, s4.z, s4.w};
-          const float bs[4] = {b4.x, b4.y, b4.z, b4.w};
-          uint16_t h[4];
+        for (int b = 0; b < 2; b++) {
+          float y[4];
 #pragma unroll
           for (int e = 0; e < 4; e++) {
-            const float y = __builtin_fmaf(static_cast<float>(v[e]), __fmul_rn(ws[e], xs), bs[e]);
-            h[e] = (OUT == kOutF16) ? f32_to_f16_rne(y) : f32_to_bf16_rne(y);
+            const int v = (BITS == 4) ? (acc[a][b][4 * g + e] >> 8) : acc[a][b][4 * g + e];
+            y[e] = __builtin_fmaf(static_cast<float>(v), __fmul_rn(ws[e], xs[b]), bs[e]);
           }
           uint2 o;
-          o.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
-          o.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Y) + (int64_t)m * N + n) = o;
+          o.x = pack2(y[0], y[1], OUT);
+          o.y = pack2(y[2], y[3], OUT);
+          const int row = b * 32 + msub;
+          const int chunk = (col >> 3) ^ (row & 15);
+          *reinterpret_cast<uint2*>(stage + row * 256 + chunk * 16 + half * 8) = o;
         }
+      }
+    }
+    // Read back whole rows: 16 lanes x 16 B = one 256-byte row segment, 4 rows per pass.
+#pragma unroll 4
+    for (int it = 0; it < 16; it++) {
+      const int row = it * 4 + (lane >> 4);
+      const int p = lane & 15;
+      const uint4 v = *reinterpret_cast<const uint4*>(stage + row * 256 + p * 16);
+      const int m = m0 + wave * 64 + row;
+      const int n = n0 + 8 * (p ^ (row & 15));
+      if (m < M && n < N) {
+        // Streaming store: Y is written once and not re-read here, so it should not evict
+        // the Wq / Xq panels that neighbouring tiles re-read from L2.
+        v4i* dst = reinterpret_cast<v4i*>(static_cast<uint16_t*>(Y) + (int64_t)m * N + n);
+        __builtin_nontemporal_store(__builtin_bit_cast(v4i, v), dst);
       }
     }
   }
