@@ -32,8 +32,11 @@
  *     rq_last_error_detail() describes the most recent failure on the calling thread.
  *   - Inputs must be finite; NaN / Inf inputs give unspecified codes.
  *   - Alignment: every tensor pointer must be 16-byte aligned.
- *   - Limits: K % 128 == 0 and 128 <= K <= 32768 (4-bit GEMM: K % 256 == 0); N % 16 == 0;
- *     M >= 0 (M == 0 is a no-op); M, N < 2^31.
+ *   - Limits: K % 128 == 0 and 128 <= K <= 131072; N % 16 == 0; M >= 0 (M == 0 is a no-op);
+ *     M, N < 2^31. The K bound keeps every int32 accumulator exact: 127^2 * K < 2^31, and the
+ *     4-bit path, which accumulates 256 * acc, has 256 * 7^2 * K < 2^31 for the codes the
+ *     quantizer emits (rq_gemm_s32 also accepts the nibble -8; a dot product in which all
+ *     131072 products are (-8) * (-8) is the one input that does not fit).
  */
 #ifndef CONVROT_H
 #define CONVROT_H

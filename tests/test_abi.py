@@ -55,6 +55,8 @@ def test_valid_arguments_pass():
     assert check(bias=None) == rq.RQ_OK
     assert check(M=0) == rq.RQ_OK
     assert check(bits=4, K=4096) == rq.RQ_OK
+    assert check(bits=4, K=384) == rq.RQ_OK
+    assert check(K=131072, N=16) == rq.RQ_OK
     assert check(x_dtype=rq.RQ_BF16, K=1536, N=4608) == rq.RQ_OK
     assert check(M=41472, K=1024, N=3072) == rq.RQ_OK
 
@@ -73,7 +75,6 @@ def test_valid_arguments_pass():
     (dict(N=1000), rq.RQ_EUNSUPPORTED),
     (dict(N=0), rq.RQ_EUNSUPPORTED),
     (dict(bits=6), rq.RQ_EUNSUPPORTED),
-    (dict(bits=4, K=384), rq.RQ_EUNSUPPORTED),                # 4-bit GEMM needs K % 256 == 0
     (dict(rot=64), rq.RQ_EUNSUPPORTED),
     (dict(kind=0), rq.RQ_EUNSUPPORTED),
     (dict(ws_bytes=100), rq.RQ_EWORKSPACE),

@@ -63,7 +63,8 @@ def test_quantize_weights_parity(key):
 
 GEMM_CASES = [(1, 16, 128, 8), (37, 48, 256, 8), (255, 272, 1024, 8), (257, 256, 384, 8),
               (600, 1040, 1024, 8), (300, 512, 4096, 8), (129, 64, 6144, 8),
-              (1, 16, 256, 4), (200, 272, 1024, 4), (517, 1024, 4096, 4)]
+              (1, 16, 128, 4), (1, 16, 256, 4), (77, 48, 384, 4), (200, 272, 1024, 4),
+              (517, 1024, 4096, 4)]
 
 
 def _random_codes(rng, rows, K, bits):

@@ -67,13 +67,11 @@ rq_status check_rows_k(int64_t rows, int64_t K, const char* what) {
   return ok();
 }
 
-rq_status check_gemm_shape(int64_t M, int64_t N, int64_t K, int bits) {
+rq_status check_gemm_shape(int64_t M, int64_t N, int64_t K) {
   rq_status s = check_rows_k(M, K, "M");
   if (s) return s;
   if (N <= 0 || N % 16 != 0 || N > kMaxRowsOrCols)
     return fail(RQ_EUNSUPPORTED, "N = %lld (need a positive multiple of 16 below 2^31)", (long long)N);
-  if (bits == 4 && K % 256 != 0)
-    return fail(RQ_EUNSUPPORTED, "4-bit GEMM needs K %% 256 == 0 (K = %lld)", (long long)K);
   return ok();
 }
 
@@ -113,7 +111,7 @@ rq_status check_linear(const void* X, int32_t x_dtype, int64_t M, int64_t K, con
   if (x_dtype != RQ_F16 && x_dtype != RQ_BF16)
     return fail(x_dtype == RQ_F32 ? RQ_EUNSUPPORTED : RQ_EINVAL,
                 "X dtype %d (supported: RQ_F16, RQ_BF16; Y has X's dtype)", x_dtype);
-  if ((s = check_gemm_shape(M, N, K, cfg->bits))) return s;
+  if ((s = check_gemm_shape(M, N, K))) return s;
   if (M == 0) return ok();
   if ((s = check_ptr(X, "X"))) return s;
   if ((s = check_ptr(Wq, "Wq"))) return s;
@@ -139,7 +137,7 @@ rq_status check_gemm(const void* Xq, const float* x_scale, const void* Wq, const
                      const void* out, int64_t out_elem) {
   rq_status s = check_cfg(cfg);
   if (s) return s;
-  if ((s = check_gemm_shape(M, N, K, cfg->bits))) return s;
+  if ((s = check_gemm_shape(M, N, K))) return s;
   if (M == 0) return ok();
   if ((s = check_ptr(Xq, "Xq"))) return s;
   if ((s = check_ptr(Wq, "Wq"))) return s;

@@ -188,68 +188,87 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
     }
   };
 
-  // One 64-byte k step from LDS stage `cur`: all 12 fragment reads first (those of slice 1
-  // interleaved with the MFMAs of slice 0), then -- when LOAD -- the 6 direct-to-LDS loads of
-  // the step two ahead, one after each MFMA. LOAD is a compile-time tag so that the whole step
-  // stays one scheduling region.
-  constexpr int kMfmaPerStep = BITS == 8 ? 16 : 32;
-  auto kstep = [&](auto load_tag, int cur, int load_stage, int load_k0) {
+  // Software-pipelined k loop over a ring of 3 LDS stages (step j lives in stage j % 3).
+  // Step kt: the slice-1 fragments of step kt are read and -- when LOAD -- the 6 direct-to-LDS
+  // loads of step kt+2 are issued under the 8 (int4: 16) MFMAs of slice 0; then -- when MID --
+  // the wave waits for its own loads of step kt+1 and for all its fragment reads, passes the
+  // workgroup barrier, and reads slice 0 of step kt+1 under the MFMAs of slice 1. LDS latency
+  // and the barrier therefore overlap matrix work instead of following it.
+  // Why the ring is race free: the loads issued in step kt fill stage (kt+2) % 3 = (kt-1) % 3,
+  // whose last reads (slice 1 of step kt-1) every wave completed before the barrier of step
+  // kt-1; the reads of stage (kt+1) % 3 follow the barrier of step kt, which every wave passes
+  // only after its loads of step kt+1 have landed.
+  constexpr int kMfmaPerSlice = BITS == 8 ? 8 : 16;
+  auto body = [&](auto load_tag, auto mid_tag, int kt, v4i (&wf0)[4], v4i (&xf0)[2]) {
     constexpr bool LOAD = decltype(load_tag)::value;
-    v4i wf[2][4], xf[2][2];
-    read_frags(cur, 0, wf[0], xf[0]);
-    read_frags(cur, 1, wf[1], xf[1]);
-    if constexpr (LOAD) issue(load_stage, load_k0);
-    mfma_slice(wf[0], xf[0]);
-    mfma_slice(wf[1], xf[1]);
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);          // slice 0 fragments
+    constexpr bool MID = decltype(mid_tag)::value;
+    const int cur = kt % kStages;
+    v4i wf1[4], xf1[2];
+    read_frags(cur, 1, wf1, xf1);
+    if constexpr (LOAD) issue((kt + 2) % kStages, (kt + 2) * kBKB);
+    mfma_slice(wf0, xf0);
 #pragma unroll
     for (int i = 0; i < 6; i++) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // DS read (slice 1)
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
     }
     if constexpr (LOAD) {
 #pragma unroll
       for (int i = 0; i < kLoadsPerStep; i++) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // VMEM (global -> LDS)
+        if (i < kMfmaPerSlice - 6) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerStep - 6 - kLoadsPerStep, 0);
-    } else {
-      __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerStep - 6, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerSlice, 0);   // the rest of slice 0
     __builtin_amdgcn_sched_barrier(0);
-  };
-  // Workgroup barrier without the memory fence of __syncthreads (which would wait for every
-  // outstanding load, draining the prefetch ring); LDS visibility of the direct loads is
-  // established by each wave's own vmcnt wait before it.
-  auto step_barrier = [&]() {
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
+    if constexpr (MID) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if constexpr (LOAD) {
+        asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags((kt + 1) % kStages, 0, wf0, xf0);
+    }
+    mfma_slice(wf1, xf1);
+    if constexpr (MID) {
+#pragma unroll
+      for (int i = 0; i < 6; i++) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read (next slice 0)
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerSlice, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Ring of 3 stages: step kt lives in stage kt % 3. At the top of step kt (when kt + 1 < nk)
-  // the loads of steps kt and kt+1 are in flight, 6 per wave each, so waiting until 6 remain
-  // lands step kt; the stage refilled during step kt (step kt+2's) was last read in step kt-1,
-  // which every wave finished before this step's barrier.
   const int nk = Kb / kBKB;
   issue(0, 0);
-  if (nk > 1) issue(1, kBKB);
-  int kt = 0;
-  for (; kt + 2 < nk; kt++) {
+  if (nk > 1) {
+    issue(1, kBKB);
     asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-    step_barrier();
-    kstep(std::true_type{}, kt % kStages, (kt + 2) % kStages, (kt + 2) * kBKB);
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
-  for (; kt < nk; kt++) {
-    if (kt + 1 < nk) {
-      asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // The epilogue operands have landed too (they were requested first): park them in LDS.
+  if constexpr (OUT != kOutS32) {
+    float* e_sw = reinterpret_cast<float*>(lds + kScaleOff);
+    if (threadIdx.x < kBN) {
+      e_sw[threadIdx.x] = my_sw;
+      e_sw[kBN + threadIdx.x] = my_b;
     }
-    step_barrier();
-    kstep(std::false_type{}, kt % kStages, 0, 0);
+    e_sw[2 * kBN + threadIdx.x] = my_sx;
   }
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  v4i wf0[4], xf0[2];
+  read_frags(0, 0, wf0, xf0);
+  int kt = 0;
+  for (; kt + 2 < nk; kt++) body(std::true_type{}, std::true_type{}, kt, wf0, xf0);
+  if (kt + 1 < nk) body(std::false_type{}, std::true_type{}, kt++, wf0, xf0);
+  body(std::false_type{}, std::false_type{}, kt, wf0, xf0);
   __syncthreads();
 
   // Epilogue. Lane l of block (a, b) holds D[n][m] for m = b*32 + l%32 and
@@ -274,29 +293,28 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
         }
     }
   } else {
-    // All of LDS is free now.
-    float* e_sw = reinterpret_cast<float*>(lds + kScaleOff);
-    float* e_b = e_sw + kBN;
-    float* e_sx = e_b + kBN;
-    if (threadIdx.x < kBN) {
-      e_sw[threadIdx.x] = my_sw;
-      e_b[threadIdx.x] = my_b;
-    }
-    e_sx[threadIdx.x] = my_sx;
-    __syncthreads();
+    // The ring is free now; the scales were parked at kScaleOff before the k loop.
+    const float* e_sw = reinterpret_cast<const float*>(lds + kScaleOff);
+    const float* e_b = e_sw + kBN;
+    const float* e_sx = e_b + kBN;
     uint8_t* stage = lds + wave * (64 * 256);     // this wave's 64 x 128 fp16 block
     float xs[2];
 #pragma unroll
     for (int b = 0; b < 2; b++) xs[b] = e_sx[wave * 64 + b * 32 + msub];
 #pragma unroll
     for (int a = 0; a < 4; a++) {
+      float4 s4[4], b4[4];
+#pragma unroll
+      for (int g = 0; g < 4; g++) {
+        const int col = a * 32 + 8 * g + 4 * half;
+        s4[g] = *reinterpret_cast<const float4*>(e_sw + col);
+        b4[g] = *reinterpret_cast<const float4*>(e_b + col);
+      }
 #pragma unroll
       for (int g = 0; g < 4; g++) {
         const int col = a * 32 + 8 * g + 4 * half;   // tile-local output column
-        const float4 s4 = *reinterpret_cast<const float4*>(e_sw + col);
-        const float4 b4 = *reinterpret_cast<const float4*>(e_b + col);
-        const float ws[4] = {s4.x, s4.y, s4.z, s4.w};
-        const float bs[4] = {b4.x, b4.y, b4.z, b4.w};
+        const float ws[4] = {s4[g].x, s4[g].y, s4[g].z, s4[g].w};
+        const float bs[4] = {b4[g].x, b4[g].y, b4[g].z, b4[g].w};
 #pragma unroll
         for (int b = 0; b < 2; b++) {
           float y[4];
@@ -314,19 +332,25 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
         }
       }
     }
-    // Read back whole rows: 16 lanes x 16 B = one 256-byte row segment, 4 rows per pass.
-#pragma unroll 4
+    // Read back whole rows (16 lanes x 16 B = one 256-byte row segment, 4 rows per read), all
+    // reads first, then the streaming stores. A wave's LDS operations complete in order, so the
+    // reads see its own writes above.
+    uint4 v[16];
+#pragma unroll
     for (int it = 0; it < 16; it++) {
       const int row = it * 4 + (lane >> 4);
-      const int p = lane & 15;
-      const uint4 v = *reinterpret_cast<const uint4*>(stage + row * 256 + p * 16);
+      v[it] = *reinterpret_cast<const uint4*>(stage + row * 256 + (lane & 15) * 16);
+    }
+#pragma unroll
+    for (int it = 0; it < 16; it++) {
+      const int row = it * 4 + (lane >> 4);
       const int m = m0 + wave * 64 + row;
-      const int n = n0 + 8 * (p ^ (row & 15));
+      const int n = n0 + 8 * ((lane & 15) ^ (row & 15));
       if (m < M && n < N) {
         // Streaming store: Y is written once and not re-read here, so it should not evict
         // the Wq / Xq panels that neighbouring tiles re-read from L2.
         v4i* dst = reinterpret_cast<v4i*>(static_cast<uint16_t*>(Y) + (int64_t)m * N + n);
-        __builtin_nontemporal_store(__builtin_bit_cast(v4i, v), dst);
+        __builtin_nontemporal_store(__builtin_bit_cast(v4i, v[it]), dst);
       }
     }
   }

@@ -7,23 +7,29 @@
 // dynamic per-token quantization). The arithmetic is fixed bit for bit (see convrot.h).
 //
 // Work layout (HBM-bound: one read of X, one write of the codes).
-//   * A row is owned by T threads (T = 16, 32, 64, 128 or 256; T/16 lanes per block-piece
-//     column); each thread holds P "pieces" of 8 consecutive elements, so K = 8 * T * P.
-//     Piece p of thread t sits at element 8 * (T*p + 16*(t/16) + j(t)): every wave-wide load
-//     is a contiguous run, and a 16-lane DPP row covers one 128-block.
-//   * Inside a lane, the 8 elements of a piece take the butterfly stages h = 1, 2, 4.
-//   * The stages h = 8, 16, 32, 64 pair pieces j and j ^ (1, 2, 4, 8). The lane->piece map
-//     j(lambda) = lambda ^ (bit2(lambda) ? 3 : 0) turns those into lane masks 1, 2, 7 and 8,
-//     which are single DPP row ops (quad_perm, quad_perm, row_half_mirror, row_ror:8).
-//   * Sign tracking: in every cross-lane stage each lane computes mine + m * partner with
+//   * A 4-lane quad owns a 128-block; lane t (0..3) of the quad holds the 4 pieces 4*i + t
+//     (i = 0..3) of 8 consecutive elements each, so element 8*(4*i + t) + r of the block has
+//     its bits r (h = 1, 2, 4) and i (h = 32, 64) inside the lane and only t (h = 8, 16)
+//     across lanes. Per load instruction a quad reads 64 contiguous bytes.
+//   * A row of nb blocks is owned by QPR = nb / BPQ quads, each holding BPQ blocks (block
+//     beta*QPR + q for quad q). Few values per lane (BPQ = 1 where possible) keep registers low
+//     and many waves resident, which is what hides the memory latency. A row takes a slot of
+//     L lanes: the next power of two of 4*QPR when that fits a wave (idle quads re-read a valid
+//     block, are left out of the absmax and store nothing), else exactly 4*QPR = 128..256 lanes
+//     over 2..4 waves that combine their absmax through LDS.
+//   * Butterfly stages in the fixed order h = 1, 2, 4 (in-lane), 8, 16 (DPP quad_perm), 32, 64
+//     (in-lane). For fp16 input the first stage also does the exact upcast: fma(x0, +-1, x1)
+//     on the two halves of a dword (v_fma_mix_f32) is the single fp32 rounding of x0 +- x1.
+//   * Sign tracking in the two cross-lane stages: each lane computes mine + m * partner with
 //     m = +1 on the lower and -1 on the upper lane of the pair. The upper lane then holds the
-//     negated butterfly difference (fl is sign-symmetric, so this is exact); after the four
-//     stages a lane's values are (-1)^popcount(j) times the true ones, which is folded into
-//     the quantizer's multiplier. Absolute values are unaffected.
+//     negated butterfly difference (fl is sign-symmetric, so this is exact); afterwards a
+//     lane's values are (-1)^popcount(t) times the true ones, which is folded into the
+//     quantizer's multiplier. Absolute values are unaffected.
 //   * Quantization: p = fl(u * inv) then fl(p + 1.5*2^23), whose low mantissa byte is the
-//     round-half-even code (|p| <= q_max << 2^22), stored straight from the bit pattern.
-// A second, generic kernel (two passes over the row: absmax, then recompute + quantize)
-// covers block counts the register-resident kernel cannot hold.
+//     round-half-even code (|p| <= q_max << 2^22), packed with byte permutes.
+// A second, generic kernel (two passes over the row: absmax, then recompute + quantize, one
+// wave per row with 16 lanes per block) covers block counts the register-resident kernel does
+// not take.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -32,12 +38,14 @@
 namespace convrot {
 namespace {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr float kInvSqrtBlock = 0x1.6a09e6p-4f;  // binary32 nearest to 1/sqrt(128)
 constexpr float kRoundMagic = 12582912.0f;       // 1.5 * 2^23
 
 template <int DPP_CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), DPP_CTRL, 0xF, 0xF, true));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), DPP_CTRL, 0xF, 0xF, true));
 }
 
 // 8 consecutive elements -> fp32 (exact upcast).
@@ -122,69 +130,165 @@ __device__ __forceinline__ float wave_max(float a, int width) {
   return a;
 }
 
-// Row absmax over the T threads of a row (T <= 64: inside the wave; else through LDS).
-__device__ __forceinline__ float row_max(float a, int T, float* red) {
-  if (T <= 64) return wave_max(a, T);
-  a = wave_max(a, 64);
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[wave] = a;
-  __syncthreads();
-  const int w0 = (threadIdx.x / T) * (T >> 6);
-  float r = red[w0];
-  for (int w = 1; w < (T >> 6); w++) r = fmaxf(r, red[w0 + w]);
-  return r;
-}
-
 __device__ __forceinline__ void row_scalars(float a, float qmax, int j, float& tinv, float& scale) {
   const float inv = (a > 0.0f) ? __fdiv_rn(qmax, a) : 0.0f;
   scale = __fdiv_rn(__fmul_rn(a, kInvSqrtBlock), qmax);
   tinv = (__builtin_popcount(j) & 1) ? -inv : inv;
 }
 
-// Register-resident kernel: P pieces per thread, T threads per row, 256 threads per block.
-template <int DT, int BITS, int P>
+// Butterfly on the two fp16 halves a (low) and b (high) of a dword, fused with the exact
+// upcast: v_fma_mix_f32 takes fp16 operands exactly and rounds a*(+-1) + b once to fp32, i.e.
+// fl(a + b) and fl(a - b). (Written out because the compiler turns fma(x, 1, y) into an add
+// and then needs separate conversions.)
+__device__ __forceinline__ void bfly_f16(uint32_t w, float& lo, float& hi) {
+  asm("v_fma_mix_f32 %0, %2, 1.0, %2 op_sel:[0,0,1] op_sel_hi:[1,0,1]\n\t"
+      "v_fma_mix_f32 %1, %2, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,1]"
+      : "=&v"(lo), "=v"(hi)
+      : "v"(w));
+}
+
+// Load piece (8 elements) and apply butterfly stage h = 1 (with the upcast).
+template <int DT>
+__device__ __forceinline__ void load_stage1(const void* base, int64_t elem, float (&v)[8]) {
+  if constexpr (DT == kF16) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + elem);
+    bfly_f16(a[0], v[0], v[1]);
+    bfly_f16(a[1], v[2], v[3]);
+    bfly_f16(a[2], v[4], v[5]);
+    bfly_f16(a[3], v[6], v[7]);
+  } else {
+    load8<DT>(base, elem, v);
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      const float a = v[i], b = v[i + 1];
+      v[i] = __fadd_rn(a, b);
+      v[i + 1] = __fsub_rn(a, b);
+    }
+  }
+}
+
+// Stages h = 2, 4 inside a piece.
+__device__ __forceinline__ void stages_2_4(float (&v)[8]) {
+#pragma unroll
+  for (int h = 2; h < 8; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      if ((i & h) == 0) {
+        const float a = v[i], b = v[i + h];
+        v[i] = __fadd_rn(a, b);
+        v[i + h] = __fsub_rn(a, b);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void bfly_pieces(float (&x)[8], float (&y)[8]) {
+#pragma unroll
+  for (int r = 0; r < 8; r++) {
+    const float a = x[r], b = y[r];
+    x[r] = __fadd_rn(a, b);
+    y[r] = __fsub_rn(a, b);
+  }
+}
+
+// Code bytes of 8 quantized values -> int8 pair of dwords or one int4 dword.
+__device__ __forceinline__ uint32_t pack4_i8(uint32_t y0, uint32_t y1, uint32_t y2, uint32_t y3) {
+  const uint32_t lo = __builtin_amdgcn_perm(y1, y0, 0x0c0c0400u);   // [y0.b0, y1.b0, 0, 0]
+  const uint32_t hi = __builtin_amdgcn_perm(y3, y2, 0x04000c0cu);   // [0, 0, y2.b0, y3.b0]
+  return lo | hi;
+}
+
+template <int BITS>
+__device__ __forceinline__ void quant_store(void* Q, int64_t elem, const float (&v)[8], float tinv) {
+  uint32_t y[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) y[i] = code_bits(v[i], tinv);
+  if constexpr (BITS == 8) {
+    uint2 o;
+    o.x = pack4_i8(y[0], y[1], y[2], y[3]);
+    o.y = pack4_i8(y[4], y[5], y[6], y[7]);
+    *reinterpret_cast<uint2*>(static_cast<int8_t*>(Q) + elem) = o;
+  } else {
+    uint32_t o = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) o |= (y[i] & 0xFu) << (4 * i);
+    *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(Q) + elem / 2) = o;
+  }
+}
+
+// Register-resident kernel: BPQ blocks per quad, QPR quads per row, rows in slots of L lanes
+// (blockDim.x = 256 with 256 / L rows per workgroup, or blockDim.x = L > 64 with one row).
+template <int DT, int BITS, int BPQ>
 __global__ __launch_bounds__(256) void rotate_quant_kernel(const void* __restrict__ X, int64_t M,
-                                                           int K, int T, void* __restrict__ Q,
+                                                           int K, int L, int qpr,
+                                                           void* __restrict__ Q,
                                                            float* __restrict__ S) {
   __shared__ float red[4];
   const int tid = threadIdx.x;
-  const int t = tid % T;
-  const int64_t row = (int64_t)blockIdx.x * (256 / T) + tid / T;
+  // L is a power of two <= 64 (256 / L rows per block) or the whole block (one row).
+  const bool one_row = L > 64;
+  const int lg = __builtin_ctz(one_row ? 64 : L);
+  const int t = one_row ? tid : (tid & (L - 1));
+  const int64_t row = one_row ? (int64_t)blockIdx.x : ((int64_t)blockIdx.x << (8 - lg)) + (tid >> lg);
   const bool active = row < M;
-  const int lam = t & 15;
-  const int j = lam ^ (((lam >> 2) & 1) * 3);
-  const int tb = t & ~15;
+  const int q = t >> 2, tq = t & 3;
+  const bool qvalid = q < qpr;
+  const int qc = qvalid ? q : qpr - 1;
   const int64_t row_elem0 = row * (int64_t)K;
+  // Rows past the end and idle quads re-read valid data (never stored): no divergent path.
+  const int64_t load_elem0 = (active ? row : M - 1) * (int64_t)K;
 
-  float v[P][8];
+  float v[BPQ][4][8];
 #pragma unroll
-  for (int p = 0; p < P; p++) {
-    if (active) {
-      load8<DT>(X, row_elem0 + 8 * (T * p + tb + j), v[p]);
-    } else {
+  for (int be = 0; be < BPQ; be++) {
+    const int64_t blk = load_elem0 + (int64_t)(be * qpr + qc) * 128;
 #pragma unroll
-      for (int i = 0; i < 8; i++) v[p][i] = 0.0f;
-    }
+    for (int i = 0; i < 4; i++) load_stage1<DT>(X, blk + 8 * (4 * i + tq), v[be][i]);
   }
-  const float m0 = (j & 1) ? -1.0f : 1.0f, m1 = (j & 2) ? -1.0f : 1.0f;
-  const float m2 = (j & 4) ? -1.0f : 1.0f, m3 = (j & 8) ? -1.0f : 1.0f;
+  const float m0 = (tq & 1) ? -1.0f : 1.0f, m1 = (tq & 2) ? -1.0f : 1.0f;
   float amax = 0.0f;
 #pragma unroll
-  for (int p = 0; p < P; p++) {
-    fwht8(v[p]);
-    cross_stages(v[p], m0, m1, m2, m3);
+  for (int be = 0; be < BPQ; be++) {
 #pragma unroll
-    for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(v[p][i]));
+    for (int i = 0; i < 4; i++) {
+      stages_2_4(v[be][i]);
+#pragma unroll
+      for (int r = 0; r < 8; r++) v[be][i][r] = __builtin_fmaf(dpp_f<0xB1>(v[be][i][r]), m0, v[be][i][r]);
+#pragma unroll
+      for (int r = 0; r < 8; r++) v[be][i][r] = __builtin_fmaf(dpp_f<0x4E>(v[be][i][r]), m1, v[be][i][r]);
+    }
+    bfly_pieces(v[be][0], v[be][1]);     // h = 32
+    bfly_pieces(v[be][2], v[be][3]);
+    bfly_pieces(v[be][0], v[be][2]);     // h = 64
+    bfly_pieces(v[be][1], v[be][3]);
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int r = 0; r < 8; r += 2) amax = fmaxf(amax, fmaxf(fabsf(v[be][i][r]), fabsf(v[be][i][r + 1])));
+  }
+  amax = qvalid ? amax : 0.0f;
+  float a;
+  if (L <= 64) {
+    a = wave_max(amax, L);
+  } else {
+    a = wave_max(amax, 64);
+    if ((tid & 63) == 0) red[tid >> 6] = a;
+    __syncthreads();
+    a = red[0];
+    for (int w = 1; w < (L >> 6); w++) a = fmaxf(a, red[w]);
   }
   const float qmax = (BITS == 8) ? 127.0f : 7.0f;
-  const float a = row_max(amax, T, red);
   float tinv, scale;
-  row_scalars(a, qmax, j, tinv, scale);
-  if (active) {
+  row_scalars(a, qmax, tq, tinv, scale);
+  if (active && qvalid) {
 #pragma unroll
-    for (int p = 0; p < P; p++) store_piece<BITS>(Q, row_elem0, 8 * (T * p + tb + j), v[p], tinv);
-    if (t == 0) S[row] = scale;
+    for (int be = 0; be < BPQ; be++) {
+      const int64_t blk = row_elem0 + (int64_t)(be * qpr + q) * 128;
+#pragma unroll
+      for (int i = 0; i < 4; i++) quant_store<BITS>(Q, blk + 8 * (4 * i + tq), v[be][i], tinv);
+    }
   }
+  if (active && t == 0) S[row] = scale;
 }
 
 // Generic two-pass kernel: one 64-thread wave per row, any number of 128-blocks. Pass 1
@@ -235,27 +339,29 @@ __global__ __launch_bounds__(256) void rotate_quant_generic_kernel(const void* _
   if (t == 0) S[row] = scale;
 }
 
-template <int DT, int BITS, int P>
-hipError_t launch_p(const void* X, int64_t M, int K, int T, void* Q, float* S, hipStream_t st) {
-  const int rows_per_block = 256 / T;
+struct RqShape {
+  int bpq;   // blocks per quad; 0 = generic kernel
+  int qpr;   // quads per row
+  int L;     // lanes per row slot
+};
+
+template <int DT, int BITS, int BPQ>
+hipError_t launch_fast(const void* X, int64_t M, int K, RqShape sh, void* Q, float* S, hipStream_t st) {
+  const int threads = sh.L <= 64 ? 256 : sh.L;
+  const int rows_per_block = threads / sh.L;
   const int64_t blocks = (M + rows_per_block - 1) / rows_per_block;
-  hipLaunchKernelGGL((rotate_quant_kernel<DT, BITS, P>), dim3((unsigned)blocks), dim3(256), 0, st,
-                     X, M, K, T, Q, S);
+  hipLaunchKernelGGL((rotate_quant_kernel<DT, BITS, BPQ>), dim3((unsigned)blocks), dim3(threads), 0,
+                     st, X, M, K, sh.L, sh.qpr, Q, S);
   return hipGetLastError();
 }
 
 template <int DT, int BITS>
-hipError_t launch_bits(const void* X, int64_t M, int K, int T, int P, void* Q, float* S,
-                       hipStream_t st) {
-  switch (P) {
-    case 1: return launch_p<DT, BITS, 1>(X, M, K, T, Q, S, st);
-    case 2: return launch_p<DT, BITS, 2>(X, M, K, T, Q, S, st);
-    case 3: return launch_p<DT, BITS, 3>(X, M, K, T, Q, S, st);
-    case 4: return launch_p<DT, BITS, 4>(X, M, K, T, Q, S, st);
-    case 5: return launch_p<DT, BITS, 5>(X, M, K, T, Q, S, st);
-    case 6: return launch_p<DT, BITS, 6>(X, M, K, T, Q, S, st);
-    case 7: return launch_p<DT, BITS, 7>(X, M, K, T, Q, S, st);
-    case 8: return launch_p<DT, BITS, 8>(X, M, K, T, Q, S, st);
+hipError_t launch_bits(const void* X, int64_t M, int K, RqShape sh, void* Q, float* S, hipStream_t st) {
+  switch (sh.bpq) {
+    case 1: return launch_fast<DT, BITS, 1>(X, M, K, sh, Q, S, st);
+    case 2: return launch_fast<DT, BITS, 2>(X, M, K, sh, Q, S, st);
+    case 3: return launch_fast<DT, BITS, 3>(X, M, K, sh, Q, S, st);
+    case 4: return launch_fast<DT, BITS, 4>(X, M, K, sh, Q, S, st);
     default: {
       const int64_t blocks = (M + 3) / 4;
       hipLaunchKernelGGL((rotate_quant_generic_kernel<DT, BITS>), dim3((unsigned)blocks),
@@ -266,42 +372,40 @@ hipError_t launch_bits(const void* X, int64_t M, int K, int T, int P, void* Q, f
 }
 
 template <int DT>
-hipError_t launch_dt(const void* X, int64_t M, int K, int bits, int T, int P, void* Q, float* S,
+hipError_t launch_dt(const void* X, int64_t M, int K, int bits, RqShape sh, void* Q, float* S,
                      hipStream_t st) {
-  return bits == 8 ? launch_bits<DT, 8>(X, M, K, T, P, Q, S, st)
-                   : launch_bits<DT, 4>(X, M, K, T, P, Q, S, st);
+  return bits == 8 ? launch_bits<DT, 8>(X, M, K, sh, Q, S, st)
+                   : launch_bits<DT, 4>(X, M, K, sh, Q, S, st);
 }
 
 }  // namespace
 
-// Threads per row T = 16 * 2^t and pieces per thread P = (K/128) / 2^t: prefer 2 <= P <= 4
-// (enough loads in flight, modest registers), else the largest T with P <= 8, else the
-// generic kernel (P = 0).
-void choose_rotate_quant_shape(int64_t K, int* T_out, int* P_out) {
+// The smallest blocks-per-quad BPQ (1..4, dividing nb) whose row fits a slot: 4*nb/BPQ lanes
+// padded to a power of two <= 64, or exactly 128, 192 or 256 lanes. Others (e.g. nb = 17)
+// take the generic kernel.
+RqShape choose_rotate_quant_shape(int64_t K) {
   const int64_t nb = K / 128;
-  int bestT = 0, bestP = 0;
-  for (int t = 0; t <= 4; t++) {
-    if (nb % (1 << t)) break;
-    const int64_t P = nb >> t;
-    if (P > 8) continue;
-    const int T = 16 << t;
-    if (bestP == 0) { bestT = T; bestP = (int)P; }
-    if (P >= 2 && P <= 4) { bestT = T; bestP = (int)P; break; }
-    if (bestP > 4 && P < bestP) { bestT = T; bestP = (int)P; }
+  for (int bpq = 1; bpq <= 4; bpq++) {
+    if (nb % bpq) continue;
+    const int64_t lanes = 4 * (nb / bpq);
+    if (lanes <= 64) {
+      int L = 4;
+      while (L < lanes) L <<= 1;
+      return {bpq, (int)(nb / bpq), L};
+    }
+    if (lanes % 64 == 0 && lanes <= 256) return {bpq, (int)(nb / bpq), (int)lanes};
   }
-  *T_out = bestT;
-  *P_out = bestP;
+  return {0, 0, 64};
 }
 
 hipError_t launch_rotate_quant(const void* X, int dt, int64_t rows, int64_t K, int bits, void* Q,
                                float* S, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
-  int T, P;
-  choose_rotate_quant_shape(K, &T, &P);
+  const RqShape sh = choose_rotate_quant_shape(K);
   switch (dt) {
-    case kF32: return launch_dt<kF32>(X, rows, (int)K, bits, T, P, Q, S, stream);
-    case kF16: return launch_dt<kF16>(X, rows, (int)K, bits, T, P, Q, S, stream);
-    default: return launch_dt<kBF16>(X, rows, (int)K, bits, T, P, Q, S, stream);
+    case kF32: return launch_dt<kF32>(X, rows, (int)K, bits, sh, Q, S, stream);
+    case kF16: return launch_dt<kF16>(X, rows, (int)K, bits, sh, Q, S, stream);
+    default: return launch_dt<kBF16>(X, rows, (int)K, bits, sh, Q, S, stream);
   }
 }
 
