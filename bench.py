@@ -16,6 +16,9 @@ breakdown. `cpu_baseline` times the CPU oracle (never tuned) on a bounded row sa
 same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+       python bench.py --copy-calibration        (a plain 1 GiB copy, for counter calibration)
+       python bench.py --pmc-summary FETCH.csv WRITE.csv COPY_FETCH.csv COPY_WRITE.csv
+                                                 (rocprofv3 counters -> profiles/pmc_traffic.json)
 """
 import argparse
 import hashlib
@@ -48,8 +51,9 @@ def kernel_source_hash():
 
 
 def traffic_from_counters(workload, kernel):
-    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE runs (scaled by a
-    copy-kernel calibration), or None if absent or taken on different kernel sources."""
+    """Memory-side bytes per launch (L2 fetch + write) of `kernel` ("gemm" or "rotate_quant")
+    from committed rocprofv3 FETCH_SIZE / WRITE_SIZE runs, scaled by a copy-kernel calibration;
+    None if absent or taken on different kernel sources."""
     try:
         with open(PMC_FILE) as fh:
             d = json.load(fh)
@@ -58,6 +62,98 @@ def traffic_from_counters(workload, kernel):
     if d.get("kernel_source_hash") != kernel_source_hash():
         return None
     return d.get("workloads", {}).get(workload, {}).get(kernel)
+
+
+COPY_BYTES = 1 << 30         # size of the plain copy that calibrates the byte counters
+
+
+def copy_calibration(reps=5):
+    """A plain device-to-device copy of COPY_BYTES (read COPY_BYTES, write COPY_BYTES), repeated;
+    run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE to scale those counters to bytes."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "reps": reps}))
+
+
+def _read_counter_csv(path):
+    """rocprofv3 counter_collection.csv -> {dispatch_id: (kernel_name, grid, {counter: value})}."""
+    import csv
+    out = {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            d = out.setdefault(int(r["Dispatch_Id"]), [r["Kernel_Name"], int(r["Grid_Size"]), {}])
+            d[2][r["Counter_Name"]] = float(r["Counter_Value"])
+    return out
+
+
+def _median_by_group(csv_path, counter, select):
+    """Median of one counter over the dispatches of each (kernel family, grid) group."""
+    import numpy as np
+    groups = {}
+    for name, grid, vals in _read_counter_csv(csv_path).values():
+        fam = select(name)
+        if fam and counter in vals:
+            groups.setdefault((fam, grid), []).append(vals[counter])
+    return {k: (float(np.median(v)), len(v)) for k, v in groups.items()}
+
+
+def pmc_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    """Reduce four rocprofv3 --pmc runs (bench FETCH_SIZE, bench WRITE_SIZE, copy FETCH_SIZE,
+    copy WRITE_SIZE; counters in KiB per dispatch) to bytes per launch of the dominant GEMM and
+    of the rotate+quantize kernel, scaled by what the same counters read for the plain copy of
+    COPY_BYTES. Writes profiles/pmc_traffic.json, keyed by the kernel sources' hash."""
+    def fam(name):
+        if "gemm_kernel" in name:
+            return "gemm"
+        if "rotate_quant" in name:
+            return "rotate_quant"
+        return None
+
+    def copy_fam(name):
+        return "copy" if "copy" in name.lower() else None
+
+    cf = _median_by_group(copy_fetch_csv, "FETCH_SIZE", copy_fam)
+    cw = _median_by_group(copy_write_csv, "WRITE_SIZE", copy_fam)
+    cf_kib = max(cf.values())[0]
+    cw_kib = max(cw.values())[0]
+    f_scale = COPY_BYTES / (cf_kib * 1024.0)
+    w_scale = COPY_BYTES / (cw_kib * 1024.0)
+    fetch = _median_by_group(fetch_csv, "FETCH_SIZE", fam)
+    write = _median_by_group(write_csv, "WRITE_SIZE", fam)
+    res = {}
+    for kind in ("gemm", "rotate_quant"):
+        # The dominant launch of each kernel is its largest grid (the largest call of the step).
+        keys = [k for k in fetch if k[0] == kind and k in write]
+        if not keys:
+            continue
+        k = max(keys, key=lambda t: t[1])
+        fb = fetch[k][0] * 1024.0 * f_scale
+        wb = write[k][0] * 1024.0 * w_scale
+        res[kind] = {"grid_threads": k[1], "dispatches": fetch[k][1], "fetch_bytes": round(fb),
+                     "write_bytes": round(wb), "bytes": round(fb + wb),
+                     "fetch_kib_raw": fetch[k][0], "write_kib_raw": write[k][0]}
+    doc = {"kernel_source_hash": kernel_source_hash(),
+           "calibration": {"copy_bytes": COPY_BYTES, "copy_fetch_kib": cf_kib, "copy_write_kib": cw_kib,
+                           "fetch_scale": f_scale, "write_scale": w_scale},
+           "workloads": {workload: res}}
+    try:
+        with open(PMC_FILE) as fh:
+            old = json.load(fh)
+        if old.get("kernel_source_hash") == doc["kernel_source_hash"]:
+            old["workloads"].update(doc["workloads"])
+            old["calibration"] = doc["calibration"]
+            doc = old
+    except (OSError, ValueError):
+        pass
+    with open(PMC_FILE, "w") as fh:
+        json.dump(doc, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(json.dumps(doc))
 
 
 def cpu_baseline(g, cfg, target_s):
@@ -85,6 +181,11 @@ def cpu_baseline(g, cfg, target_s):
                       "epilogue); %.1f s" % (rows, cfg.M, t)}
 
 
+def synth_workload_name(key):
+    from w4a4_integer_quantized_amd import synth
+    return synth.CONFIGS[key].workload
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -93,7 +194,17 @@ def main():
     ap.add_argument("--workload", default="vit_attn")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="reduce rocprofv3 counter CSVs into profiles/pmc_traffic.json (no GPU)")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(synth_workload_name(args.workload), *args.pmc_summary)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the quantized linear "
               "shards over tokens with no exchange; see the design notes). Run with --gpus 1.")
@@ -131,7 +242,7 @@ def main():
     set_bytes = x_host.numel() * 2
     for lin in cfg.linears:
         set_bytes += M * lin.N * 2 + rq.workspace_size(M, lin.K, bits)
-    R = max(2, min(8, math.ceil(3 * MALL_BYTES / set_bytes)))
+    R = max(3, min(8, math.ceil(3 * MALL_BYTES / set_bytes)))
     sets = []
     for _ in range(R):
         s = {"X": x_host.to(dev), "Y": {}, "ws": {}}
@@ -206,8 +317,9 @@ def main():
     torch.cuda.synchronize()
     calls = {}
     for c, lin in enumerate(cfg.linears):
-        rq_ms = sum(ev[i][3 * c].elapsed_time(ev[i][3 * c + 1]) for i in range(args.steps)) / args.steps
-        gm_ms = sum(ev[i][3 * c + 1].elapsed_time(ev[i][3 * c + 2]) for i in range(args.steps)) / args.steps
+        rq_t = np.array([ev[i][3 * c].elapsed_time(ev[i][3 * c + 1]) for i in range(args.steps)])
+        gm_t = np.array([ev[i][3 * c + 1].elapsed_time(ev[i][3 * c + 2]) for i in range(args.steps)])
+        rq_ms, gm_ms = float(rq_t.mean()), float(gm_t.mean())
         ops = 2 * M * lin.N * lin.K
         rq_bytes = M * lin.K * 2 + M * lin.K * bits // 8 + 4 * M
         gemm_bytes = M * lin.K * bits // 8 + lin.N * lin.K * bits // 8 + 8 * lin.N + 4 * M + M * lin.N * 2
@@ -222,19 +334,25 @@ def main():
             "call_TOPS": round(ops / ((rq_ms + gm_ms) * 1e-3) / 1e12, 1),
             "call_int8_peak_frac": round(ops / ((rq_ms + gm_ms) * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
             "rotate_quant_alg_bytes": rq_bytes, "gemm_alg_bytes": gemm_bytes, "gemm_alg_ops": ops,
+            "rotate_quant_us_p10_p50_p90": [round(float(np.percentile(rq_t, p)) * 1e3, 2) for p in (10, 50, 90)],
+            "gemm_us_p10_p50_p90": [round(float(np.percentile(gm_t, p)) * 1e3, 2) for p in (10, 50, 90)],
         }
     dom = max(cfg.linears, key=lambda l: l.N * l.K)
     dc = calls[dom.name]
-    traffic = traffic_from_counters(args.workload, "gemm_" + dom.name)
+    tr = traffic_from_counters(cfg.workload, "gemm")
+    traffic = tr["bytes"] if tr else None
     roofline = {"bound": "mfma", "kernel": "gemm_kernel (%s: %dx%dx%d, W%dA%d)" % (dom.name, M, dom.N, dom.K, bits, bits),
                 "achieved": dc["gemm_TOPS"], "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
                 "frac": dc["gemm_mfma_frac"], "traffic": traffic,
-                "avg_launch_us": dc["gemm_us"], "alg_ops_per_launch": dc["gemm_alg_ops"]}
-    rq_traffic = traffic_from_counters(args.workload, "rotate_quant_" + dom.name)
+                "avg_launch_us": dc["gemm_us"], "alg_ops_per_launch": dc["gemm_alg_ops"],
+                "alg_bytes_per_launch": dc["gemm_alg_bytes"], "traffic_detail": tr}
+    rtr = traffic_from_counters(cfg.workload, "rotate_quant")
+    rq_traffic = rtr["bytes"] if rtr else None
     roofline_rq = {"bound": "hbm", "kernel": "rotate_quant_kernel (%s input %dx%d)" % (dom.name, M, dom.K),
                    "achieved": dc["rotate_quant_GBps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                    "frac": dc["rotate_quant_hbm_frac"], "traffic": rq_traffic,
-                   "avg_launch_us": dc["rotate_quant_us"], "alg_bytes_per_launch": dc["rotate_quant_alg_bytes"]}
+                   "avg_launch_us": dc["rotate_quant_us"], "alg_bytes_per_launch": dc["rotate_quant_alg_bytes"],
+                   "traffic_detail": rtr}
 
     out = {
         "metric": "rotq_linear TOPS (rotate+quant+GEMM) and % of MI355X INT8 MFMA peak",
