@@ -354,6 +354,19 @@ def main():
                    "avg_launch_us": dc["rotate_quant_us"], "alg_bytes_per_launch": dc["rotate_quant_alg_bytes"],
                    "traffic_detail": rtr}
 
+    # Quantization error as context (not parity): GPU outputs on a row sample against the
+    # unquantized linear X W^T + b in float64 (plain numpy), relative Frobenius norm.
+    qerr = {}
+    rs = np.random.default_rng(12345).choice(M, min(M, 512), replace=False)
+    for lin in cfg.linears:
+        xs_bits = g["x_bits"] if lin.source == "x" else None
+        if xs_bits is None:
+            continue          # second-layer inputs come from the GPU's own GELU; skip
+        xr = torch.from_numpy(xs_bits[rs].view(np.int16)).view(tdt).float().numpy().astype(np.float64)
+        ref = xr @ g["W"][lin.name].astype(np.float64).T + g["bias"][lin.name].astype(np.float64)
+        got = sets[0]["Y"][lin.name][torch.from_numpy(rs).to(dev)].float().cpu().numpy().astype(np.float64)
+        qerr[lin.name] = round(float(np.linalg.norm(got - ref) / np.linalg.norm(ref)), 6)
+
     out = {
         "metric": "rotq_linear TOPS (rotate+quant+GEMM) and % of MI355X INT8 MFMA peak",
         "value": round(tops, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
@@ -364,6 +377,7 @@ def main():
         "int8_peak_frac": round(tops / PEAK_INT8_TOPS, 4),
         "roofline": roofline, "roofline_rotate_quant": roofline_rq, "calls": calls,
         "weight_quant_ms_offline": round(wq_ms, 3), "buffer_sets": R,
+        "quant_error_rel_frobenius_vs_fp64": qerr,
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle, ~%.0f s)" % args.cpu_seconds)
