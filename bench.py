@@ -44,7 +44,7 @@ def log(msg):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("gemm_i8.hip", "rotate_quant.hip"):
+    for f in ("gemm_i8.hip", "gemm_i8_wide.hip", "rotate_quant.hip"):
         with open(os.path.join(ROOT, "w4a4_integer_quantized_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -257,12 +257,18 @@ def main():
 
     def lin_input(s, lin):
         if lin.source == "x":
-            return s["X"]
-        # MLP pair: the second layer's input is GELU of the first layer's output (torch op on the
-        # GPU, outside the library)
-        first = cfg.linears[0].name
-        approx = "tanh" if lin.source == "gelu_tanh" else "none"
-        return torch.nn.functional.gelu(s["Y"][first], approximate=approx)
+            X = s["X"]
+        else:
+            # MLP pair: the second layer's input is GELU of its producer's output (torch op on
+            # the GPU, outside the library)
+            approx = "tanh" if lin.source == "gelu_tanh" else "none"
+            X = torch.nn.functional.gelu(s["Y"][lin.producer], approximate=approx)
+        # The raw entry points take bare pointers: check every buffer's shape on the host first.
+        assert X.shape == (M, lin.K) and X.dtype == tdt and X.is_contiguous(), (lin.name, X.shape)
+        assert s["Y"][lin.name].shape == (M, lin.N), lin.name
+        assert s["ws"][lin.name].numel() >= rq.workspace_size(M, lin.K, bits), lin.name
+        assert Wq[lin.name].shape == rq.code_shape(lin.N, lin.K, bits), lin.name
+        return X
 
     def step(i):
         s = sets[i % R]

@@ -110,6 +110,42 @@ def test_gemm_dequant_parity(M, N, K, bits, io, with_bias):
     assert np.array_equal(got, ref)
 
 
+# Shapes the launcher sends to its 256 x 256-tile kernel (K of at least 1536 bytes of codes and
+# at least 192 such tiles), ragged in M and N; compared on sampled rows (all N columns).
+WIDE_CASES = [(2048, 6144, 1536, 8), (1900, 6160, 1536, 8), (2000, 6144, 3072, 4)]
+
+
+def _sample_rows(M, seed):
+    rng = np.random.default_rng(seed)
+    rows = set(range(40)) | set(range(M - 40, M)) | set(int(r) for r in rng.choice(M, 48, replace=False))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+@pytest.mark.parametrize("M,N,K,bits", WIDE_CASES)
+def test_gemm_wide_tiles_parity(M, N, K, bits):
+    need_gpu()
+    assert ((M + 255) // 256) * ((N + 255) // 256) >= 192 and K * bits // 8 >= 1536
+    rng = np.random.default_rng(M + N + K + bits)
+    A = _random_codes(rng, M, K, bits)
+    B = _random_codes(rng, N, K, bits)
+    rows = _sample_rows(M, M + 1)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    Ad, Bd = dev(oracle.pack_codes(A, bits)), dev(oracle.pack_codes(B, bits))
+    acc = rq.gemm_s32(Ad, Bd, bits=bits, K=K)
+    sx = (rng.random(M) * 0.05).astype(np.float32)
+    sw = (rng.random(N) * 2e-4).astype(np.float32)
+    b = rng.normal(0, 0.01, N).astype(np.float32)
+    ys = {io: rq.gemm_dequant(Ad, dev(sx), Bd, dev(sw), dev(b), bits=bits, K=K,
+                              out_dtype=torch.float16 if io == "f16" else torch.bfloat16)
+          for io in ("f16", "bf16")}
+    torch.cuda.synchronize()
+    ref_acc = oracle.gemm_s32(A[rows], B)
+    assert np.array_equal(acc.cpu().numpy()[rows], ref_acc)
+    for io, Y in ys.items():
+        ref = oracle.epilogue(ref_acc, sx[rows], sw, b, IO_CODE[io])
+        assert np.array_equal(bits_from_dev(Y)[rows], ref), io
+
+
 def _linear_case(xb, io, W, b, bits):
     Wd = dev_from_bits(W, "f32")
     Wq, ws = rq.quantize_weights(Wd, bits=bits)

@@ -16,12 +16,14 @@
 //   * K is staged 64 bytes per step (64 int8 or 128 int4 codes) through a 3-deep LDS ring
 //     filled by direct global->LDS 16-byte loads (prefetch distance 2 steps). Rows are 64 B;
 //     the 16-byte chunk c of row r sits at c ^ swz(r), which keeps the MFMA fragment reads
-//     (ds_read_b128, 32 rows x 2 chunks per wave) free of bank conflicts for 32- and 64-bank
-//     layouts alike.
+//     (ds_read_b128, 32 rows x 2 chunks per wave) free of bank conflicts on gfx950's LDS
+//     (see swz). The fragment reads of the next slice are issued between the MFMAs of the
+//     current one, MFMA first, so no wave waits on a read it has just issued.
 //   * The MFMA "A" operand is a Wq row block and "B" an Xq row block, so each lane ends with
 //     4 consecutive output columns of one token. The epilogue converts them and parks the
-//     wave's 64 x 128 output block in LDS (16-byte chunks XOR-swizzled by row), then writes it
-//     back as full 256-byte row segments with 16-byte stores. w_scale, bias and x_scale for the
+//     wave's 64 x 128 output block in LDS (16-byte chunks XOR-swizzled by row, 8-byte halves
+//     swapped on rows with bit 4 set, which makes the 8-byte writes conflict free), then
+//     writes it back as full 256-byte row segments with 16-byte stores. w_scale, bias and x_scale for the
 //     tile are loaded at kernel start (latency hidden behind the mainloop) and read from LDS.
 //   * INT4: a 16-byte chunk of packed codes (32 nibbles) becomes two MFMA operands,
 //     (w << 4) & 0xF0F0F0F0 (even k) and w & 0xF0F0F0F0 (odd k): each byte is 16 * code,
@@ -56,7 +58,10 @@ constexpr int kLoadsPerStep = kStageBytes / 1024 / 4;   // wave-wide 1 KB copies
 
 enum OutKind { kOutS32 = 0, kOutF16 = 1, kOutBF16 = 2 };
 
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// gfx950 LDS: 64 banks of 4 bytes, 16 lanes of a ds_read_b128 per cycle, and address bit 9
+// flips bank bit 5 (measured with the bank-conflict counter). With 64-byte rows that hardware
+// hash already separates rows r and r + 8, so the swizzle only spreads rows r..r+7 (bits 1-2).
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 3; }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -209,8 +214,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
     mfma_slice(wf0, xf0);
 #pragma unroll
     for (int i = 0; i < 6; i++) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // DS read (slice 1)
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // DS read (slice 1)
     }
     if constexpr (LOAD) {
 #pragma unroll
@@ -236,8 +241,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
     if constexpr (MID) {
 #pragma unroll
       for (int i = 0; i < 6; i++) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read (next slice 0)
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read (next slice 0)
       }
     }
     __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerSlice, 0);
@@ -328,7 +333,10 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
           o.y = pack2(y[2], y[3], OUT);
           const int row = b * 32 + msub;
           const int chunk = (col >> 3) ^ (row & 15);
-          *reinterpret_cast<uint2*>(stage + row * 256 + chunk * 16 + half * 8) = o;
+          // Rows r and r + 16 share a chunk position; their 8-byte halves are swapped so the
+          // 32 lanes of a write hit distinct banks (undone when the row is read back).
+          const int hpos = half ^ ((row >> 4) & 1);
+          *reinterpret_cast<uint2*>(stage + row * 256 + chunk * 16 + hpos * 8) = o;
         }
       }
     }
@@ -340,6 +348,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
     for (int it = 0; it < 16; it++) {
       const int row = it * 4 + (lane >> 4);
       v[it] = *reinterpret_cast<const uint4*>(stage + row * 256 + (lane & 15) * 16);
+      // Rows with bit 4 set hold their 8-byte halves swapped (see the writes); bit 4 of row is
+      // (it >> 2) & 1 for every lane, so this is a compile-time register swap.
+      if ((it >> 2) & 1) v[it] = make_uint4(v[it].z, v[it].w, v[it].x, v[it].y);
     }
 #pragma unroll
     for (int it = 0; it < 16; it++) {
@@ -376,6 +387,13 @@ hipError_t launch_gemm(const void* Xq, const float* sx, const void* Wq, const fl
                        int out_dt, int32_t* acc32, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   const int64_t Kb = bits == 8 ? K : K / 2;
+  // Kernel choice, from timings of both kernels on MI355X over the workloads' shapes: this
+  // kernel (two 256 x 128 workgroups per CU, each one's epilogue hidden behind the other's
+  // k loop) is faster or equal everywhere except long K on enough tiles to fill the machine,
+  // where the 256 x 256 kernel's lower operand traffic per MFMA wins (by up to ~20%).
+  const int64_t wide_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (wide_gemm_supported(Kb) && Kb >= 1536 && wide_tiles >= 192)
+    return launch_gemm_wide(Xq, sx, Wq, sw, bias, M, N, K, bits, Y, out_dt, acc32, stream);
   if (acc32) {
     return bits == 8 ? launch<8, kOutS32>(Xq, sx, Wq, sw, bias, M, N, Kb, acc32, stream)
                      : launch<4, kOutS32>(Xq, sx, Wq, sw, bias, M, N, Kb, acc32, stream);

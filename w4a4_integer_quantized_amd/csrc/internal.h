@@ -19,4 +19,11 @@ hipError_t launch_gemm(const void* Xq, const float* sx, const void* Wq, const fl
                        const float* bias, int64_t M, int64_t N, int64_t K, int bits,
                        void* Y, int out_dt, int32_t* acc32, hipStream_t stream);
 
+// The same GEMM on 256 x 256 tiles with 128-byte k steps (launch_gemm picks it for long K);
+// it needs Kb (K in bytes of codes) to be a multiple of 128 and at least 256.
+bool wide_gemm_supported(int64_t Kb);
+hipError_t launch_gemm_wide(const void* Xq, const float* sx, const void* Wq, const float* sw,
+                            const float* bias, int64_t M, int64_t N, int64_t K, int bits,
+                            void* Y, int out_dt, int32_t* acc32, hipStream_t stream);
+
 }  // namespace convrot

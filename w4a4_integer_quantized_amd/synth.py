@@ -42,6 +42,7 @@ class Linear:
     N: int                 # output features (rows of W)
     K: int                 # input features
     source: str            # "x" (the config's X) or "gelu_erf" / "gelu_tanh" (second layer)
+    producer: str = ""     # second layer: the linear whose output (through GELU) feeds this one
 
 
 @dataclasses.dataclass(frozen=True)
@@ -63,7 +64,7 @@ CONFIGS: Dict[str, Config] = {
     "single": Config("single", "w8a8_single_linear_256x1024x1024", 0, 256, 1024, "normal", 8, 50.0,
                  "f16", 8, (Linear("linear", 1024, 1024, "x"),)),
     "vit_mlp": Config("vit_mlp", "vitl_mlp_pair_b1_5184x1024x4096", 1, 5184, 1024, "normal", 10, 30.0,
-                 "f16", 8, (Linear("fc1", 4096, 1024, "x"), Linear("fc2", 1024, 4096, "gelu_erf"))),
+                 "f16", 8, (Linear("fc1", 4096, 1024, "x"), Linear("fc2", 1024, 4096, "gelu_erf", "fc1"))),
     "vit_attn": Config("vit_attn", "vitl_attn_proj_b8_41472x1024_qkv3072_oproj1024", 2, 41472, 1024,
                  "normal", 8, 50.0, "f16", 8,
                  (Linear("qkv", 3072, 1024, "x"), Linear("oproj", 1024, 1024, "x"))),
@@ -71,8 +72,22 @@ CONFIGS: Dict[str, Config] = {
                  "f16", 4, (Linear("linear", 1024, 4096, "x"),)),
     "dit": Config("dit", "dit_block_bf16_8192x1536", 4, 8192, 1536, "normal", 16, 50.0, "bf16", 8,
                  (Linear("qkv", 4608, 1536, "x"), Linear("w1", 6144, 1536, "x"),
-                  Linear("w2", 1536, 6144, "gelu_tanh"))),
+                  Linear("w2", 1536, 6144, "gelu_tanh", "w1"))),
 }
+
+
+def _check_configs():
+    for cfg in CONFIGS.values():
+        names = {lin.name: lin for lin in cfg.linears}
+        for lin in cfg.linears:
+            if lin.source == "x":
+                assert lin.K == cfg.K and not lin.producer, (cfg.key, lin.name)
+            else:
+                prod = names[lin.producer]
+                assert prod.source == "x" and prod.N == lin.K, (cfg.key, lin.name)
+
+
+_check_configs()
 
 
 def f32_to_bf16_bits_rne(x: np.ndarray) -> np.ndarray:
