@@ -173,12 +173,24 @@ def cpu_baseline(g, cfg, target_s):
             ops += 2 * rows * lin.N * lin.K
         return time.perf_counter() - t0, ops
 
-    t, _ = run(16)
-    rows = int(min(cfg.M, max(16, 16 * target_s / max(t, 1e-6))))
-    t, ops = run(rows)
-    return {"value": ops / t / 1e12, "unit": "TOPS", "cores": oracle.num_threads(), "kind": "oracle",
+    # Grow the token sample until one pass takes a tenth of the target (or covers the whole
+    # step), then repeat passes until the target time is spent.
+    rows = min(cfg.M, 256)
+    while True:
+        t, ops = run(rows)
+        if rows == cfg.M or t >= 0.1 * target_s:
+            break
+        rows = int(min(cfg.M, max(2 * rows, rows * 0.1 * target_s / max(t, 1e-6))))
+    total_t, total_ops, passes = t, ops, 1
+    while total_t < target_s:
+        t, ops = run(rows)
+        total_t += t
+        total_ops += ops
+        passes += 1
+    return {"value": total_ops / total_t / 1e12, "unit": "TOPS", "cores": oracle.num_threads(),
+            "kind": "oracle",
             "sample": "first %d of %d tokens, every linear of the step (rotate+quantize, int GEMM, "
-                      "epilogue); %.1f s" % (rows, cfg.M, t)}
+                      "epilogue), %d passes, %.1f s" % (rows, cfg.M, passes, total_t)}
 
 
 def synth_workload_name(key):

@@ -45,6 +45,9 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBM = 256;                       // tokens per tile
 constexpr int kBN = 256;                       // output features per tile
@@ -87,22 +90,15 @@ __device__ __forceinline__ v4i read_frag(const uint8_t* lds_tile, int row, int c
   return *reinterpret_cast<const v4i*>(lds_tile + row * kBKB + ((chunk ^ swz(row)) << 4));
 }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
-  uint32_t u = __float_as_uint(v);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
-}
-
 // The epilogue rounds twice by definition: fma -> binary32, then binary32 -> fp16/bf16. The
 // empty asm pins each value as a binary32 register so the compiler cannot fuse the conversion
 // into the fma (v_fma_mix* rounds once, straight to fp16, which differs on rare ties).
+// gfx950 converts a pair with one v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32 (round to nearest even).
 __device__ __forceinline__ uint32_t pack2(float a, float b, int out) {
   asm volatile("" : "+v"(a), "+v"(b));
-  if (out == kOutF16) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<_Float16>(a)) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, static_cast<_Float16>(b)) << 16);
-  }
-  return (uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16);
+  const f32x2 v = {a, b};
+  if (out == kOutF16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 template <int BITS, int OUT>
