@@ -7,24 +7,24 @@
 // dynamic per-token quantization). The arithmetic is fixed bit for bit (see convrot.h).
 //
 // Work layout (HBM-bound: one read of X, one write of the codes).
-//   * A 4-lane quad owns a 128-block; lane t (0..3) of the quad holds the 4 pieces 4*i + t
-//     (i = 0..3) of 8 consecutive elements each, so element 8*(4*i + t) + r of the block has
-//     its bits r (h = 1, 2, 4) and i (h = 32, 64) inside the lane and only t (h = 8, 16)
-//     across lanes. Per load instruction a quad reads 64 contiguous bytes.
+//   * A 4-lane quad owns a 128-block; lane t (0..3) of the quad holds the 32 consecutive
+//     elements 32*t .. 32*t + 31 as 4 pieces of 8, so element 32*t + 8*i + r of the block has
+//     its bits r (h = 1, 2, 4) and i (h = 8, 16) inside the lane and only t (h = 32, 64)
+//     across lanes. Each lane then stores its 32 codes as one contiguous run (16-byte stores),
+//     which measured faster than interleaving the quad's pieces.
 //   * A row of nb blocks is owned by QPR = nb / BPQ quads, each holding BPQ blocks (block
 //     beta*QPR + q for quad q). Few values per lane (BPQ = 1 where possible) keep registers low
 //     and many waves resident, which is what hides the memory latency. A row takes a slot of
 //     L lanes: the next power of two of 4*QPR when that fits a wave (idle quads re-read a valid
 //     block, are left out of the absmax and store nothing), else exactly 4*QPR = 128..256 lanes
 //     over 2..4 waves that combine their absmax through LDS.
-//   * Butterfly stages in the fixed order h = 1, 2, 4 (in-lane), 8, 16 (DPP quad_perm), 32, 64
-//     (in-lane). For fp16 input the first stage also does the exact upcast: fma(x0, +-1, x1)
+//   * Butterfly stages in the fixed order h = 1, 2, 4, 8, 16 (in-lane), 32, 64 (DPP quad_perm). For fp16 input the first stage also does the exact upcast: fma(x0, +-1, x1)
 //     on the two halves of a dword (v_fma_mix_f32) is the single fp32 rounding of x0 +- x1.
 //   * Sign tracking in the two cross-lane stages: each lane computes mine + m * partner with
 //     m = +1 on the lower and -1 on the upper lane of the pair. The upper lane then holds the
-//     negated butterfly difference (fl is sign-symmetric, so this is exact); afterwards a
-//     lane's values are (-1)^popcount(t) times the true ones, which is folded into the
-//     quantizer's multiplier. Absolute values are unaffected.
+//     negated butterfly difference (fl is sign-symmetric, so this is exact); a lane's values are
+//     then (-1)^popcount(t) times the true ones (the second stage pairs lanes with equal sign
+//     factors), which is folded into the quantizer's multiplier. Absolute values are unaffected.
 //   * Quantization: p = fl(u * inv) then fl(p + 1.5*2^23), whose low mantissa byte is the
 //     round-half-even code (|p| <= q_max << 2^22), packed with byte permutes.
 // A second, generic kernel (two passes over the row: absmax, then recompute + quantize, one
@@ -198,21 +198,31 @@ __device__ __forceinline__ uint32_t pack4_i8(uint32_t y0, uint32_t y1, uint32_t 
   return lo | hi;
 }
 
+// Quantize + store the 32 consecutive codes of v[0..3] (elements elem .. elem + 31).
 template <int BITS>
-__device__ __forceinline__ void quant_store(void* Q, int64_t elem, const float (&v)[8], float tinv) {
-  uint32_t y[8];
+__device__ __forceinline__ void quant_store32(void* Q, int64_t elem, const float (&v)[4][8], float tinv) {
+  uint32_t w[8];
 #pragma unroll
-  for (int i = 0; i < 8; i++) y[i] = code_bits(v[i], tinv);
+  for (int i = 0; i < 4; i++) {
+    uint32_t y[8];
+#pragma unroll
+    for (int r = 0; r < 8; r++) y[r] = code_bits(v[i][r], tinv);
+    if constexpr (BITS == 8) {
+      w[2 * i] = pack4_i8(y[0], y[1], y[2], y[3]);
+      w[2 * i + 1] = pack4_i8(y[4], y[5], y[6], y[7]);
+    } else {
+      uint32_t o = 0;
+#pragma unroll
+      for (int r = 0; r < 8; r++) o |= (y[r] & 0xFu) << (4 * r);
+      w[i] = o;
+    }
+  }
   if constexpr (BITS == 8) {
-    uint2 o;
-    o.x = pack4_i8(y[0], y[1], y[2], y[3]);
-    o.y = pack4_i8(y[4], y[5], y[6], y[7]);
-    *reinterpret_cast<uint2*>(static_cast<int8_t*>(Q) + elem) = o;
+    uint4* p = reinterpret_cast<uint4*>(static_cast<int8_t*>(Q) + elem);
+    p[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    p[1] = make_uint4(w[4], w[5], w[6], w[7]);
   } else {
-    uint32_t o = 0;
-#pragma unroll
-    for (int i = 0; i < 8; i++) o |= (y[i] & 0xFu) << (4 * i);
-    *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(Q) + elem / 2) = o;
+    *reinterpret_cast<uint4*>(static_cast<uint8_t*>(Q) + elem / 2) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -243,24 +253,26 @@ __global__ __launch_bounds__(256) void rotate_quant_kernel(const void* __restric
   for (int be = 0; be < BPQ; be++) {
     const int64_t blk = load_elem0 + (int64_t)(be * qpr + qc) * 128;
 #pragma unroll
-    for (int i = 0; i < 4; i++) load_stage1<DT>(X, blk + 8 * (4 * i + tq), v[be][i]);
+    for (int i = 0; i < 4; i++) load_stage1<DT>(X, blk + 32 * tq + 8 * i, v[be][i]);
   }
   const float m0 = (tq & 1) ? -1.0f : 1.0f, m1 = (tq & 2) ? -1.0f : 1.0f;
   float amax = 0.0f;
 #pragma unroll
   for (int be = 0; be < BPQ; be++) {
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      stages_2_4(v[be][i]);
-#pragma unroll
-      for (int r = 0; r < 8; r++) v[be][i][r] = __builtin_fmaf(dpp_f<0xB1>(v[be][i][r]), m0, v[be][i][r]);
-#pragma unroll
-      for (int r = 0; r < 8; r++) v[be][i][r] = __builtin_fmaf(dpp_f<0x4E>(v[be][i][r]), m1, v[be][i][r]);
-    }
-    bfly_pieces(v[be][0], v[be][1]);     // h = 32
+    for (int i = 0; i < 4; i++) stages_2_4(v[be][i]);
+    bfly_pieces(v[be][0], v[be][1]);     // h = 8
     bfly_pieces(v[be][2], v[be][3]);
-    bfly_pieces(v[be][0], v[be][2]);     // h = 64
+    bfly_pieces(v[be][0], v[be][2]);     // h = 16
     bfly_pieces(v[be][1], v[be][3]);
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int r = 0; r < 8; r++) v[be][i][r] = __builtin_fmaf(dpp_f<0xB1>(v[be][i][r]), m0, v[be][i][r]);   // h = 32
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int r = 0; r < 8; r++) v[be][i][r] = __builtin_fmaf(dpp_f<0x4E>(v[be][i][r]), m1, v[be][i][r]);   // h = 64
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
@@ -282,11 +294,8 @@ __global__ __launch_bounds__(256) void rotate_quant_kernel(const void* __restric
   row_scalars(a, qmax, tq, tinv, scale);
   if (active && qvalid) {
 #pragma unroll
-    for (int be = 0; be < BPQ; be++) {
-      const int64_t blk = row_elem0 + (int64_t)(be * qpr + q) * 128;
-#pragma unroll
-      for (int i = 0; i < 4; i++) quant_store<BITS>(Q, blk + 8 * (4 * i + tq), v[be][i], tinv);
-    }
+    for (int be = 0; be < BPQ; be++)
+      quant_store32<BITS>(Q, row_elem0 + (int64_t)(be * qpr + q) * 128 + 32 * tq, v[be], tinv);
   }
   if (active && t == 0) S[row] = scale;
 }
