@@ -264,6 +264,7 @@ def main():
         sets.append(s)
     log("ring of %d buffer sets, %.0f MB each" % (R, set_bytes / 1e6))
     cfgc = rq.make_cfg(bits)
+    cfg_tiled = rq.make_cfg(bits, x_layout=rq.RQ_X_TILED)
     xdt = rq.RQ_F16 if cfg.io == "f16" else rq.RQ_BF16
     sptr = stream.cuda_stream
 
@@ -308,7 +309,8 @@ def main():
     log("timed %d steps: %.3f ms/step, %.1f TOPS" % (args.steps, ms_per_step, tops))
 
     # Per-kernel durations: the same two kernels per call (rotate+quantize, GEMM+epilogue)
-    # launched through the split entry points, with HIP events between them on the stream.
+    # launched through the split entry points with the fused call's tiled code layout, with
+    # HIP events between them on the stream.
     nl = len(cfg.linears)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3 * nl)] for _ in range(args.steps)]
 
@@ -316,13 +318,14 @@ def main():
         s = sets[i % R]
         for c, lin in enumerate(cfg.linears):
             X = lin_input(s, lin)
-            xq = s["ws"][lin.name].data_ptr()                        # workspace = [Xq | x_scale]
-            xs = xq + (M * lin.K * bits // 8 + 255) // 256 * 256
+            # The fused call's own layout: workspace = [tiled Xq | x_scale].
+            xq = s["ws"][lin.name].data_ptr()
+            xs = xq + (rq.rq_codes_bytes(M, lin.K, cfg_tiled) + 255) // 256 * 256
             evs[3 * c].record(stream)
-            st = rq.rq_rotate_quantize(X.data_ptr(), xdt, M, lin.K, cfgc, xq, xs, sptr)
+            st = rq.rq_rotate_quantize(X.data_ptr(), xdt, M, lin.K, cfg_tiled, xq, xs, sptr)
             evs[3 * c + 1].record(stream)
             st |= rq.rq_gemm_dequant(xq, xs, Wq[lin.name].data_ptr(), Ws[lin.name].data_ptr(),
-                                     B[lin.name].data_ptr(), M, lin.N, lin.K, cfgc,
+                                     B[lin.name].data_ptr(), M, lin.N, lin.K, cfg_tiled,
                                      s["Y"][lin.name].data_ptr(), xdt, sptr)
             evs[3 * c + 2].record(stream)
             assert st == rq.RQ_OK

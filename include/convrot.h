@@ -18,6 +18,14 @@
  *              code = round_half_even(fl(u * inv)); q_max = 127 (8-bit) or 7 (4-bit).
  *   storage    8-bit: int8 [rows, K]; 4-bit: uint8 [rows, K/2], two's-complement nibbles,
  *              low nibble = even k.
+ *   activation code layouts (rq_qconfig.x_layout; weights are always row-major):
+ *              RQ_X_ROWS   row-major as above, rows * Kb bytes (Kb = K or K/2 bytes per row);
+ *              RQ_X_TILED  the GEMM's tile order: 256-row panels, each split into 64-byte
+ *                          k steps stored as [panel][step][256 rows][64 B]. Byte b of row m
+ *                          sits at ((m / 256 * (Kb / 64) + b / 64) * 256 + m % 256) * 64 + b % 64.
+ *                          Rows are padded to a multiple of 256 (pad rows hold no defined value
+ *                          and are never used); rq_codes_bytes() gives the size. The GEMM's
+ *                          operand loads are then whole contiguous 1 KB blocks.
  *   epilogue   y = fma(f32(acc), fl(w_scale[n] * x_scale[m]), bias[n] or +0), rounded to
  *              nearest-even fp16 / bf16.
  *
@@ -60,11 +68,20 @@ typedef enum { RQ_F32 = 0, RQ_F16 = 1, RQ_BF16 = 2 } rq_dtype;
 
 enum { RQ_ROT_WHT = 1 };   /* normalized Walsh-Hadamard rotation, Sylvester order */
 
+enum { RQ_X_ROWS = 0, RQ_X_TILED = 1 };   /* activation code layouts (see above) */
+
 typedef struct {
   int32_t bits;       /* 8 (W8A8) or 4 (W4A4) */
   int32_t rot_kind;   /* must be RQ_ROT_WHT */
   int32_t rot_block;  /* must be 128 */
+  int32_t x_layout;   /* RQ_X_ROWS or RQ_X_TILED: layout of Xq in rq_rotate_quantize,
+                         rq_gemm_dequant and rq_gemm_s32 (rq_quantize_weights ignores it;
+                         rq_rotq_linear always uses RQ_X_TILED inside its workspace) */
 } rq_qconfig;
+
+/* Bytes of activation codes for `rows` rows of length K in cfg's bits and x_layout
+ * (0 if cfg is invalid or the sizes are out of range). */
+size_t rq_codes_bytes(int64_t rows, int64_t K, const rq_qconfig *cfg);
 
 /* Offline weight quantizer ("Quantization recipe": upcast to FP32, block-Hadamard transform,
  * per-row scales).
@@ -79,13 +96,15 @@ rq_status rq_quantize_weights(const void *W, int32_t w_dtype, int64_t N, int64_t
  * same arithmetic as rq_quantize_weights ("What ConvRot changes": the matching rotation is
  * applied to activations at run time; "Quantization recipe": dynamic activation quantization).
  *   X        [M, K] device, dtype x_dtype (RQ_F32, RQ_F16 or RQ_BF16)
- *   Xq       out: int8 [M, K] (bits 8) or uint8 [M, K/2] (bits 4)
+ *   Xq       out: rq_codes_bytes(M, K, cfg) bytes in cfg->x_layout: int8 [M, K] (bits 8) or
+ *            uint8 [M, K/2] (bits 4) row-major, or the tiled layout
  *   x_scale  out: float [M] (one scale per token) */
 rq_status rq_rotate_quantize(const void *X, int32_t x_dtype, int64_t M, int64_t K,
                              const rq_qconfig *cfg, void *Xq, float *x_scale, void *stream);
 
-/* Bytes of device workspace rq_rotq_linear needs: Xq followed by x_scale, each rounded up to
- * 256 bytes. Returns 0 if cfg is invalid. */
+/* Bytes of device workspace rq_rotq_linear needs: Xq in RQ_X_TILED layout
+ * (rq_codes_bytes(M, K) with x_layout = RQ_X_TILED) followed by x_scale [M], each rounded up
+ * to 256 bytes. Returns 0 if cfg is invalid. */
 size_t rq_rotq_linear_workspace_size(int64_t M, int64_t K, const rq_qconfig *cfg);
 
 /* The quantized linear ("Quantization recipe": W8A8 / W4A4 operations with online activation
@@ -103,7 +122,8 @@ rq_status rq_rotq_linear(const void *X, int32_t x_dtype, int64_t M, int64_t K,
                          void *stream);
 
 /* The GEMM + epilogue alone (the second kernel of rq_rotq_linear).
- *   Xq [M, K] int8 / [M, K/2] uint8, x_scale [M]; Wq, w_scale, bias as above;
+ *   Xq codes of M rows in cfg->x_layout (as rq_rotate_quantize writes them), x_scale [M];
+ *   Wq, w_scale, bias as above;
  *   Y  out: [M, N] of y_dtype (RQ_F16 or RQ_BF16). */
 rq_status rq_gemm_dequant(const void *Xq, const float *x_scale, const void *Wq,
                           const float *w_scale, const float *bias, int64_t M, int64_t N,
@@ -111,7 +131,7 @@ rq_status rq_gemm_dequant(const void *Xq, const float *x_scale, const void *Wq,
                           void *stream);
 
 /* Same mainloop, storing the exact int32 accumulators acc[M, N] = sum_k Xq[m,k] * Wq[n,k]
- * (for bit-exact checks). */
+ * (for bit-exact checks); Xq in cfg->x_layout. */
 rq_status rq_gemm_s32(const void *Xq, const void *Wq, int64_t M, int64_t N, int64_t K,
                       const rq_qconfig *cfg, int32_t *acc, void *stream);
 

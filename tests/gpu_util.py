@@ -64,3 +64,27 @@ def y_tolerance_ok(y_gpu_bits, y_ref_bits, io):
     assert np.array_equal(np.isfinite(a), fin)
     err = np.abs(a[fin] - b[fin])
     return bool(np.all(err <= 1e-3 + 2.0**-9 * np.abs(b[fin]))), float(err.max(initial=0.0))
+
+
+def _tiled_index(M, Kb):
+    """For the tiled activation-code layout ([256-row panel][64-byte k step][256 rows][64 B],
+    rows padded to whole panels), the flat byte index of every (row, byte) of an [M, Kb] array."""
+    m = np.arange(M, dtype=np.int64)[:, None]
+    b = np.arange(Kb, dtype=np.int64)[None, :]
+    return (((m // 256) * (Kb // 64) + b // 64) * 256 + m % 256) * 64 + b % 64
+
+
+def untile_codes(flat: np.ndarray, M: int, K: int, bits: int) -> np.ndarray:
+    """Tiled code bytes -> row-major [M, Kb] (int8 for 8-bit, uint8 packed for 4-bit)."""
+    Kb = K if bits == 8 else K // 2
+    out = np.asarray(flat).view(np.uint8)[_tiled_index(M, Kb)]
+    return out.view(np.int8) if bits == 8 else out
+
+
+def tile_codes(rowmajor: np.ndarray, M: int, K: int, bits: int, pad_fill: int = 0x5A) -> np.ndarray:
+    """Row-major code bytes [M, Kb] -> tiled flat buffer; pad rows get `pad_fill`."""
+    Kb = K if bits == 8 else K // 2
+    Mp = (M + 255) // 256 * 256
+    out = np.full(Mp * Kb, pad_fill, dtype=np.uint8)
+    out[_tiled_index(M, Kb)] = np.ascontiguousarray(rowmajor).view(np.uint8).reshape(M, Kb)
+    return out

@@ -35,7 +35,8 @@ def test_status_strings():
 
 
 def _args(**kw):
-    cfg = rq.make_cfg(kw.pop("bits", 8), kw.pop("rot", 128), kw.pop("kind", rq.RQ_ROT_WHT))
+    cfg = rq.make_cfg(kw.pop("bits", 8), kw.pop("rot", 128), kw.pop("kind", rq.RQ_ROT_WHT),
+                      kw.pop("x_layout", rq.RQ_X_ROWS))
     M, K, N = kw.pop("M", 256), kw.pop("K", 1024), kw.pop("N", 1024)
     base = dict(X=A, x_dtype=rq.RQ_F16, M=M, K=K, Wq=A + 4 * GB, w_scale=A + 8 * GB, N=N,
                 bias=A + 9 * GB, cfg=cfg, Y=A + 12 * GB, ws=A + 20 * GB,
@@ -76,6 +77,7 @@ def test_valid_arguments_pass():
     (dict(N=0), rq.RQ_EUNSUPPORTED),
     (dict(bits=6), rq.RQ_EUNSUPPORTED),
     (dict(rot=64), rq.RQ_EUNSUPPORTED),
+    (dict(x_layout=2), rq.RQ_EINVAL),
     (dict(kind=0), rq.RQ_EUNSUPPORTED),
     (dict(ws_bytes=100), rq.RQ_EWORKSPACE),
     (dict(Y=A + 100 * 2), rq.RQ_EINVAL),                      # Y overlaps X
@@ -88,12 +90,29 @@ def test_invalid_arguments_rejected(kw, status):
 
 
 def test_workspace_size():
+    # Tiled codes: rows padded to whole 256-row panels, then x_scale; each part 256-byte aligned.
     cfg8, cfg4 = rq.make_cfg(8), rq.make_cfg(4)
     assert rq.rq_rotq_linear_workspace_size(256, 1024, cfg8) == 256 * 1024 + 1024
-    assert rq.rq_rotq_linear_workspace_size(5184, 4096, cfg4) == 5184 * 2048 + 5184 * 4
-    assert rq.rq_rotq_linear_workspace_size(5, 256, cfg4) == 768 + 256
-    assert rq.rq_rotq_linear_workspace_size(3, 128, cfg8) == 512 + 256
+    assert rq.rq_rotq_linear_workspace_size(5184, 4096, cfg4) == 5376 * 2048 + 5184 * 4
+    assert rq.rq_rotq_linear_workspace_size(5, 256, cfg4) == 256 * 128 + 256
+    assert rq.rq_rotq_linear_workspace_size(3, 128, cfg8) == 256 * 128 + 256
+    assert rq.rq_rotq_linear_workspace_size(0, 1024, cfg8) == 0
     assert rq.rq_rotq_linear_workspace_size(3, 128, rq.make_cfg(5)) == 0
+    # The layout field of cfg does not change the fused call's workspace.
+    assert rq.rq_rotq_linear_workspace_size(300, 1024, rq.make_cfg(8, x_layout=rq.RQ_X_TILED)) == \
+        rq.rq_rotq_linear_workspace_size(300, 1024, cfg8)
+
+
+def test_codes_bytes():
+    rows, tiled = rq.make_cfg(8), rq.make_cfg(8, x_layout=rq.RQ_X_TILED)
+    assert rq.rq_codes_bytes(300, 1024, rows) == 300 * 1024
+    assert rq.rq_codes_bytes(300, 1024, tiled) == 512 * 1024
+    assert rq.rq_codes_bytes(256, 1024, tiled) == 256 * 1024
+    assert rq.rq_codes_bytes(1, 4096, rq.make_cfg(4, x_layout=rq.RQ_X_TILED)) == 256 * 2048
+    assert rq.rq_codes_bytes(7, 4096, rq.make_cfg(4)) == 7 * 2048
+    assert rq.rq_codes_bytes(0, 1024, tiled) == 0
+    assert rq.rq_codes_bytes(5, 1000, rows) == 0                       # K % 128 != 0
+    assert rq.rq_codes_bytes(5, 1024, rq.make_cfg(8, x_layout=2)) == 0  # bad layout
 
 
 def test_entry_points_reject_before_launch():
@@ -117,3 +136,11 @@ def test_tensor_wrappers_refuse_host_tensors():
     import torch
     with pytest.raises(ValueError):
         rq.rotate_quantize(torch.zeros(4, 128, dtype=torch.float16))
+
+
+def test_qconfig_struct_matches_header():
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct \{(.*?)\} rq_qconfig;", text, re.S).group(1)
+    fields = re.findall(r"int32_t\s+(\w+);", body)
+    assert [f for f, _ in rq.rq_qconfig._fields_] == fields
+    assert ctypes.sizeof(rq.rq_qconfig) == 4 * len(fields)

@@ -2,7 +2,7 @@
 benchmark times (rq_rotq_linear with a caller-provided workspace), plus size edge cases.
 
 Full size: every activation code and per-token scale (read back from the workspace, whose
-layout is Xq then x_scale, each padded to 256 bytes) and every weight code and scale is
+layout is the tiled Xq then x_scale, each padded to 256 bytes) and every weight code and scale is
 compared with the CPU oracle; the output Y is compared on a sample of rows (the first and
 last rows, the rows around a 256-row tile edge, the ragged last tile and random rows) for
 which the oracle runs the whole linear, all N columns. Properties that hold for every row
@@ -16,7 +16,7 @@ import oracle
 import w4a4_integer_quantized_amd as rq
 from w4a4_integer_quantized_amd import synth
 from tests.gpu_util import (IO_CODE, bits_from_dev, codes_np, compare_codes, dev_from_bits,
-                            need_gpu, y_tolerance_ok)
+                            need_gpu, untile_codes, y_tolerance_ok)
 
 pytestmark = pytest.mark.gpu
 
@@ -73,11 +73,11 @@ def test_full_size_linear(key):
         Y = rq.rotq_linear(X, Wq, ws, bd, bits=bits, workspace=wsbuf)
         torch.cuda.synchronize()
 
-        # Every activation code and scale.
-        cb = M * K * bits // 8
-        xq = wsbuf[:cb].view(torch.int8 if bits == 8 else torch.uint8).view(M, K * bits // 8)
+        # Every activation code and scale (the workspace holds the codes in the tiled layout).
+        cb = rq.rq_codes_bytes(M, K, rq.make_cfg(bits, x_layout=rq.RQ_X_TILED))
         xs = wsbuf[_round256(cb):_round256(cb) + 4 * M].view(torch.float32)
-        xq_np, xs_np = codes_np(xq), xs.cpu().numpy()
+        xq_np = untile_codes(wsbuf[:cb].cpu().numpy(), M, K, bits)
+        xs_np = xs.cpu().numpy()
         ref_c, ref_s, ref_p = oracle.quantize_rows(xb, IO_CODE[io], bits, want_pre=True)
         nmis = compare_codes(xq_np, ref_c, ref_p, bits, K)
         assert np.array_equal(xs_np.view(np.uint32), ref_s.view(np.uint32)), lin.name
@@ -93,7 +93,7 @@ def test_full_size_linear(key):
             assert np.array_equal(got, ref["Y"]), lin.name
         print("  %s: K=%d N=%d codes %d mismatches, Y rows bit-exact=%s" %
               (lin.name, K, N, nmis, bool(np.array_equal(got, ref["Y"]))), flush=True)
-        del X, Y, wsbuf, xq, xs
+        del X, Y, wsbuf, xs
         torch.cuda.empty_cache()
 
 

@@ -13,7 +13,7 @@ import oracle
 import w4a4_integer_quantized_amd as rq
 from w4a4_integer_quantized_amd import synth
 from tests.gpu_util import (IO_CODE, bits_from_dev, codes_np, compare_codes, dev_from_bits,
-                            need_gpu, y_tolerance_ok)
+                            need_gpu, tile_codes, untile_codes, y_tolerance_ok)
 
 pytestmark = pytest.mark.gpu
 
@@ -46,6 +46,26 @@ def test_rotate_quantize_parity(K, M, io, bits):
     ref_c, ref_s, ref_p = oracle.quantize_rows(xb, IO_CODE[io], bits, want_pre=True)
     compare_codes(codes_np(Xq), ref_c, ref_p, bits, K)
     assert np.array_equal(xs.cpu().numpy().view(np.uint32), ref_s.view(np.uint32))
+
+
+@pytest.mark.parametrize("K,M", [(128, 1), (384, 33), (1024, 300), (1536, 257), (2176, 11),
+                                 (4096, 70), (6144, 19)])
+@pytest.mark.parametrize("io,bits", [("f16", 8), ("bf16", 8), ("f16", 4)])
+def test_rotate_quantize_tiled_layout(K, M, io, bits):
+    """The tiled activation-code layout holds exactly the row-major codes (and the oracle's)."""
+    need_gpu()
+    xb, _ = _rows(K + M + bits + 7, M, K, io, zero_rows=(0,) if M > 1 else ())
+    Xd = dev_from_bits(xb, io)
+    Xt, st = rq.rotate_quantize(Xd, bits=bits, x_layout=rq.RQ_X_TILED)
+    Xr, sr = rq.rotate_quantize(Xd, bits=bits)
+    torch.cuda.synchronize()
+    assert Xt.numel() == rq.rq_codes_bytes(M, K, rq.make_cfg(bits, x_layout=rq.RQ_X_TILED))
+    got = untile_codes(Xt.cpu().numpy(), M, K, bits)
+    assert np.array_equal(got.view(np.uint8), codes_np(Xr).view(np.uint8))
+    assert torch.equal(st, sr)
+    ref_c, ref_s, ref_p = oracle.quantize_rows(xb, IO_CODE[io], bits, want_pre=True)
+    compare_codes(got, ref_c, ref_p, bits, K)
+    assert np.array_equal(st.cpu().numpy().view(np.uint32), ref_s.view(np.uint32))
 
 
 @pytest.mark.parametrize("key", list(synth.CONFIGS))
@@ -85,6 +105,27 @@ def test_gemm_s32_parity(M, N, K, bits):
     acc = rq.gemm_s32(Ad, Bd, bits=bits, K=K)
     torch.cuda.synchronize()
     assert np.array_equal(acc.cpu().numpy(), oracle.gemm_s32(A, B))
+
+
+@pytest.mark.parametrize("M,N,K,bits", GEMM_CASES)
+def test_gemm_tiled_layout_parity(M, N, K, bits):
+    """GEMM on tiled activation codes (pad rows filled with garbage, which must not matter)."""
+    need_gpu()
+    rng = np.random.default_rng(M * N + K + 17)
+    A = _random_codes(rng, M, K, bits)
+    B = _random_codes(rng, N, K, bits)
+    At = torch.from_numpy(tile_codes(oracle.pack_codes(A, bits), M, K, bits, pad_fill=0x77)).cuda()
+    Bd = torch.from_numpy(oracle.pack_codes(B, bits)).cuda()
+    acc = rq.gemm_s32(At, Bd, bits=bits, K=K, x_layout=rq.RQ_X_TILED, M=M)
+    sx = (rng.random(M) * 0.05).astype(np.float32)
+    sw = (rng.random(N) * 2e-4).astype(np.float32)
+    b = rng.normal(0, 0.01, N).astype(np.float32)
+    dev = lambda a: torch.from_numpy(a).cuda()
+    Y = rq.gemm_dequant(At, dev(sx), Bd, dev(sw), dev(b), bits=bits, K=K, x_layout=rq.RQ_X_TILED)
+    torch.cuda.synchronize()
+    ref_acc = oracle.gemm_s32(A, B)
+    assert np.array_equal(acc.cpu().numpy(), ref_acc)
+    assert np.array_equal(bits_from_dev(Y), oracle.epilogue(ref_acc, sx, sw, b, oracle.F16))
 
 
 @pytest.mark.parametrize("M,N,K,bits", GEMM_CASES[::2])

@@ -22,6 +22,7 @@ _LIB_PATH = os.path.join(PKG, "libconvrot.so")
 RQ_OK, RQ_EINVAL, RQ_EUNSUPPORTED, RQ_EWORKSPACE, RQ_EHIP = range(5)
 RQ_F32, RQ_F16, RQ_BF16 = 0, 1, 2
 RQ_ROT_WHT = 1
+RQ_X_ROWS, RQ_X_TILED = 0, 1
 
 
 class ConvRotError(RuntimeError):
@@ -31,7 +32,8 @@ class ConvRotError(RuntimeError):
 
 
 class rq_qconfig(ctypes.Structure):
-    _fields_ = [("bits", ctypes.c_int32), ("rot_kind", ctypes.c_int32), ("rot_block", ctypes.c_int32)]
+    _fields_ = [("bits", ctypes.c_int32), ("rot_kind", ctypes.c_int32), ("rot_block", ctypes.c_int32),
+                ("x_layout", ctypes.c_int32)]
 
 
 _lib = None
@@ -67,6 +69,8 @@ def load():
         f.restype = ctypes.c_int
     lib.rq_rotq_linear_workspace_size.argtypes = [I64, I64, CFG]
     lib.rq_rotq_linear_workspace_size.restype = SZ
+    lib.rq_codes_bytes.argtypes = [I64, I64, CFG]
+    lib.rq_codes_bytes.restype = SZ
     lib.rq_status_string.argtypes = [ctypes.c_int]
     lib.rq_status_string.restype = ctypes.c_char_p
     lib.rq_last_error_detail.argtypes = []
@@ -89,8 +93,9 @@ def _check(status: int, where: str):
         raise ConvRotError(status, where, load().rq_last_error_detail().decode())
 
 
-def make_cfg(bits: int = 8, rot_block: int = 128, rot_kind: int = RQ_ROT_WHT) -> rq_qconfig:
-    return rq_qconfig(bits, rot_kind, rot_block)
+def make_cfg(bits: int = 8, rot_block: int = 128, rot_kind: int = RQ_ROT_WHT,
+             x_layout: int = RQ_X_ROWS) -> rq_qconfig:
+    return rq_qconfig(bits, rot_kind, rot_block, x_layout)
 
 
 # ----------------------------------------------------------------------------- raw entry points
@@ -118,6 +123,10 @@ def rq_gemm_s32(Xq, Wq, M, N, K, cfg, acc, stream) -> int:
 
 def rq_rotq_linear_workspace_size(M, K, cfg) -> int:
     return load().rq_rotq_linear_workspace_size(M, K, ctypes.byref(cfg))
+
+
+def rq_codes_bytes(rows, K, cfg) -> int:
+    return load().rq_codes_bytes(rows, K, ctypes.byref(cfg))
 
 
 def rq_check_rotq_linear_args(X, x_dtype, M, K, Wq, w_scale, N, bias, cfg, Y, ws, ws_bytes) -> int:
@@ -179,13 +188,18 @@ def quantize_weights(W, bits: int = 8, rot: int = 128, stream=None):
     return Wq, ws
 
 
-def rotate_quantize(X, bits: int = 8, rot: int = 128, stream=None):
-    """Online step alone: X [M, K] -> (Xq, x_scale f32 [M])."""
+def rotate_quantize(X, bits: int = 8, rot: int = 128, stream=None, x_layout: int = RQ_X_ROWS):
+    """Online step alone: X [M, K] -> (Xq, x_scale f32 [M]). Xq is [M, K] int8 / [M, K/2] uint8
+    (RQ_X_ROWS) or a flat uint8 buffer of rq_codes_bytes() in the tiled layout (RQ_X_TILED)."""
     torch = _torch()
     M, K = X.shape
-    Xq = torch.empty(code_shape(M, K, bits), dtype=torch.int8 if bits == 8 else torch.uint8, device=X.device)
+    cfg = make_cfg(bits, rot, x_layout=x_layout)
+    if x_layout == RQ_X_ROWS:
+        Xq = torch.empty(code_shape(M, K, bits), dtype=torch.int8 if bits == 8 else torch.uint8, device=X.device)
+    else:
+        Xq = torch.empty((max(rq_codes_bytes(M, K, cfg), 1),), dtype=torch.uint8, device=X.device)
     xs = torch.empty((M,), dtype=torch.float32, device=X.device)
-    _check(rq_rotate_quantize(_dev(X, "X"), _dtype_code(X), M, K, make_cfg(bits, rot),
+    _check(rq_rotate_quantize(_dev(X, "X"), _dtype_code(X), M, K, cfg,
                               Xq.data_ptr(), xs.data_ptr(), _stream(stream)), "rq_rotate_quantize")
     return Xq, xs
 
@@ -209,25 +223,29 @@ def rotq_linear(X, Wq, w_scale, bias=None, bits: int = 8, rot: int = 128, worksp
 
 
 def gemm_dequant(Xq, x_scale, Wq, w_scale, bias=None, bits: int = 8, K: Optional[int] = None,
-                 out_dtype=None, stream=None):
+                 out_dtype=None, stream=None, x_layout: int = RQ_X_ROWS):
+    """Y [M, N] from codes; M = len(x_scale), K from Wq unless given."""
     torch = _torch()
-    M = Xq.shape[0]
+    M = x_scale.shape[0]
     N = Wq.shape[0]
-    K = K if K is not None else (Xq.shape[1] if bits == 8 else 2 * Xq.shape[1])
+    K = K if K is not None else (Wq.shape[1] if bits == 8 else 2 * Wq.shape[1])
     out_dtype = torch.float16 if out_dtype is None else out_dtype
     Y = torch.empty((M, N), dtype=out_dtype, device=Xq.device)
     _check(rq_gemm_dequant(_dev(Xq, "Xq"), _dev(x_scale, "x_scale"), _dev(Wq, "Wq"), _dev(w_scale, "w_scale"),
-                           _dev(bias, "bias") if bias is not None else None, M, N, K, make_cfg(bits),
-                           Y.data_ptr(), _dtype_code(Y), _stream(stream)), "rq_gemm_dequant")
+                           _dev(bias, "bias") if bias is not None else None, M, N, K,
+                           make_cfg(bits, x_layout=x_layout), Y.data_ptr(), _dtype_code(Y),
+                           _stream(stream)), "rq_gemm_dequant")
     return Y
 
 
-def gemm_s32(Xq, Wq, bits: int = 8, K: Optional[int] = None, stream=None):
+def gemm_s32(Xq, Wq, bits: int = 8, K: Optional[int] = None, stream=None,
+             x_layout: int = RQ_X_ROWS, M: Optional[int] = None):
+    """acc [M, N] int32; M = Xq.shape[0] for row-major codes (give M for the tiled layout)."""
     torch = _torch()
-    M = Xq.shape[0]
+    M = Xq.shape[0] if M is None else M
     N = Wq.shape[0]
-    K = K if K is not None else (Xq.shape[1] if bits == 8 else 2 * Xq.shape[1])
+    K = K if K is not None else (Wq.shape[1] if bits == 8 else 2 * Wq.shape[1])
     acc = torch.empty((M, N), dtype=torch.int32, device=Xq.device)
-    _check(rq_gemm_s32(_dev(Xq, "Xq"), _dev(Wq, "Wq"), M, N, K, make_cfg(bits), acc.data_ptr(),
-                       _stream(stream)), "rq_gemm_s32")
+    _check(rq_gemm_s32(_dev(Xq, "Xq"), _dev(Wq, "Wq"), M, N, K, make_cfg(bits, x_layout=x_layout),
+                       acc.data_ptr(), _stream(stream)), "rq_gemm_s32")
     return acc

@@ -39,6 +39,12 @@ int64_t elem_size(int32_t dt) { return dt == RQ_F32 ? 4 : 2; }
 
 int64_t code_bytes(int64_t rows, int64_t K, int bits) { return bits == 8 ? rows * K : rows * K / 2; }
 
+// Activation codes in a layout: the tiled layout pads the rows to whole 256-row panels.
+int64_t x_code_bytes(int64_t rows, int64_t K, int bits, int32_t layout) {
+  const int64_t r = layout == RQ_X_TILED ? (rows + 255) / 256 * 256 : rows;
+  return code_bytes(r, K, bits);
+}
+
 int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
 
 bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
@@ -55,6 +61,8 @@ rq_status check_cfg(const rq_qconfig* cfg) {
     return fail(RQ_EUNSUPPORTED, "rot_kind = %d (supported: RQ_ROT_WHT)", cfg->rot_kind);
   if (cfg->rot_block != 128)
     return fail(RQ_EUNSUPPORTED, "rot_block = %d (supported: 128)", cfg->rot_block);
+  if (cfg->x_layout != RQ_X_ROWS && cfg->x_layout != RQ_X_TILED)
+    return fail(RQ_EINVAL, "x_layout = %d (RQ_X_ROWS or RQ_X_TILED)", cfg->x_layout);
   return ok();
 }
 
@@ -87,7 +95,7 @@ rq_status from_hip(hipError_t e, const char* where) {
 }
 
 rq_status check_rotate_args(const void* X, int32_t dt, int64_t rows, int64_t K, const rq_qconfig* cfg,
-                            const void* Q, const float* S, const char* xname) {
+                            const void* Q, const float* S, const char* xname, bool activations) {
   rq_status s = check_cfg(cfg);
   if (s) return s;
   if (dt != RQ_F32 && dt != RQ_F16 && dt != RQ_BF16) return fail(RQ_EINVAL, "bad %s dtype %d", xname, dt);
@@ -97,7 +105,8 @@ rq_status check_rotate_args(const void* X, int32_t dt, int64_t rows, int64_t K, 
   if ((s = check_ptr(Q, "codes output"))) return s;
   if (!S) return fail(RQ_EINVAL, "scale output is NULL");
   if ((reinterpret_cast<uintptr_t>(S) & 3u) != 0) return fail(RQ_EINVAL, "scale output is not 4-byte aligned");
-  const int64_t xb = rows * K * elem_size(dt), qb = code_bytes(rows, K, cfg->bits);
+  const int64_t xb = rows * K * elem_size(dt);
+  const int64_t qb = activations ? x_code_bytes(rows, K, cfg->bits, cfg->x_layout) : code_bytes(rows, K, cfg->bits);
   if (overlap(X, xb, Q, qb) || overlap(X, xb, S, rows * 4) || overlap(Q, qb, S, rows * 4))
     return fail(RQ_EINVAL, "input, codes and scales must not overlap");
   return ok();
@@ -147,7 +156,8 @@ rq_status check_gemm(const void* Xq, const float* x_scale, const void* Wq, const
   if ((s = check_ptr(bias, "bias", false))) return s;
   if (out_elem != 4 && !x_scale) return fail(RQ_EINVAL, "x_scale is NULL");
   const int64_t ob = M * N * out_elem;
-  if (overlap(out, ob, Xq, code_bytes(M, K, cfg->bits)) || overlap(out, ob, Wq, code_bytes(N, K, cfg->bits)) ||
+  if (overlap(out, ob, Xq, x_code_bytes(M, K, cfg->bits, cfg->x_layout)) ||
+      overlap(out, ob, Wq, code_bytes(N, K, cfg->bits)) ||
       overlap(out, ob, x_scale, M * 4) || overlap(out, ob, w_scale, N * 4) || overlap(out, ob, bias, N * 4))
     return fail(RQ_EINVAL, "output overlaps an input");
   return ok();
@@ -174,23 +184,30 @@ const char* rq_version(void) { return "0.1.0"; }
 
 size_t rq_rotq_linear_workspace_size(int64_t M, int64_t K, const rq_qconfig* cfg) {
   if (check_cfg(cfg) != RQ_OK || M < 0 || K <= 0) return 0;
-  return (size_t)(round256(code_bytes(M, K, cfg->bits)) + round256(M * 4));
+  return (size_t)(round256(x_code_bytes(M, K, cfg->bits, RQ_X_TILED)) + round256(M * 4));
+}
+
+size_t rq_codes_bytes(int64_t rows, int64_t K, const rq_qconfig* cfg) {
+  if (check_cfg(cfg) != RQ_OK || rows < 0 || rows > kMaxRowsOrCols || K <= 0 || K > kMaxK || K % 128)
+    return 0;
+  return (size_t)x_code_bytes(rows, K, cfg->bits, cfg->x_layout);
 }
 
 rq_status rq_quantize_weights(const void* W, int32_t w_dtype, int64_t N, int64_t K,
                               const rq_qconfig* cfg, void* Wq, float* w_scale, void* stream) {
-  rq_status s = check_rotate_args(W, w_dtype, N, K, cfg, Wq, w_scale, "W");
+  rq_status s = check_rotate_args(W, w_dtype, N, K, cfg, Wq, w_scale, "W", false);
   if (s) return s;
-  return from_hip(convrot::launch_rotate_quant(W, w_dtype, N, K, cfg->bits, Wq, w_scale,
+  return from_hip(convrot::launch_rotate_quant(W, w_dtype, N, K, cfg->bits, false, Wq, w_scale,
                                                static_cast<hipStream_t>(stream)),
                   "rotate_quant launch");
 }
 
 rq_status rq_rotate_quantize(const void* X, int32_t x_dtype, int64_t M, int64_t K,
                              const rq_qconfig* cfg, void* Xq, float* x_scale, void* stream) {
-  rq_status s = check_rotate_args(X, x_dtype, M, K, cfg, Xq, x_scale, "X");
+  rq_status s = check_rotate_args(X, x_dtype, M, K, cfg, Xq, x_scale, "X", true);
   if (s) return s;
-  return from_hip(convrot::launch_rotate_quant(X, x_dtype, M, K, cfg->bits, Xq, x_scale,
+  return from_hip(convrot::launch_rotate_quant(X, x_dtype, M, K, cfg->bits,
+                                               cfg->x_layout == RQ_X_TILED, Xq, x_scale,
                                                static_cast<hipStream_t>(stream)),
                   "rotate_quant launch");
 }
@@ -209,12 +226,13 @@ rq_status rq_rotq_linear(const void* X, int32_t x_dtype, int64_t M, int64_t K, c
   rq_status s = check_linear(X, x_dtype, M, K, Wq, w_scale, N, bias, cfg, Y, workspace, ws_bytes);
   if (s || M == 0) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  // The workspace holds the codes in the tiled layout, then x_scale.
   uint8_t* Xq = static_cast<uint8_t*>(workspace);
-  float* sx = reinterpret_cast<float*>(Xq + round256(code_bytes(M, K, cfg->bits)));
-  if ((s = from_hip(convrot::launch_rotate_quant(X, x_dtype, M, K, cfg->bits, Xq, sx, st),
+  float* sx = reinterpret_cast<float*>(Xq + round256(x_code_bytes(M, K, cfg->bits, RQ_X_TILED)));
+  if ((s = from_hip(convrot::launch_rotate_quant(X, x_dtype, M, K, cfg->bits, true, Xq, sx, st),
                     "rotate_quant launch")))
     return s;
-  return from_hip(convrot::launch_gemm(Xq, sx, Wq, w_scale, bias, M, N, K, cfg->bits, Y,
+  return from_hip(convrot::launch_gemm(Xq, sx, Wq, w_scale, bias, M, N, K, cfg->bits, true, Y,
                                        x_dtype, nullptr, st),
                   "gemm launch");
 }
@@ -227,8 +245,9 @@ rq_status rq_gemm_dequant(const void* Xq, const float* x_scale, const void* Wq,
     return fail(y_dtype == RQ_F32 ? RQ_EUNSUPPORTED : RQ_EINVAL, "Y dtype %d (supported: RQ_F16, RQ_BF16)", y_dtype);
   rq_status s = check_gemm(Xq, x_scale, Wq, w_scale, bias, M, N, K, cfg, Y, 2);
   if (s || M == 0) return s;
-  return from_hip(convrot::launch_gemm(Xq, x_scale, Wq, w_scale, bias, M, N, K, cfg->bits, Y,
-                                       y_dtype, nullptr, static_cast<hipStream_t>(stream)),
+  return from_hip(convrot::launch_gemm(Xq, x_scale, Wq, w_scale, bias, M, N, K, cfg->bits,
+                                       cfg->x_layout == RQ_X_TILED, Y, y_dtype, nullptr,
+                                       static_cast<hipStream_t>(stream)),
                   "gemm launch");
 }
 
@@ -237,7 +256,8 @@ rq_status rq_gemm_s32(const void* Xq, const void* Wq, int64_t M, int64_t N, int6
   rq_status s = check_gemm(Xq, nullptr, Wq, nullptr, nullptr, M, N, K, cfg, acc, 4);
   if (s || M == 0) return s;
   return from_hip(convrot::launch_gemm(Xq, nullptr, Wq, nullptr, nullptr, M, N, K, cfg->bits,
-                                       acc, RQ_F16, acc, static_cast<hipStream_t>(stream)),
+                                       cfg->x_layout == RQ_X_TILED, acc, RQ_F16, acc,
+                                       static_cast<hipStream_t>(stream)),
                   "gemm launch");
 }
 

@@ -98,7 +98,7 @@ __device__ __forceinline__ uint32_t pack2(float a, float b, int out) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-template <int BITS, int OUT>
+template <int BITS, int OUT, bool XT>
 __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
     const uint8_t* __restrict__ Xq, const float* __restrict__ sx, const uint8_t* __restrict__ Wq,
     const float* __restrict__ sw, const float* __restrict__ bias, void* __restrict__ Y, int M,
@@ -140,7 +140,19 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
     uint8_t* tX = lds + stage * kStageBytes;
     uint8_t* tW = tX + kTileX;
 #pragma unroll
-    for (int i = 0; i < 4; i++) copy_rows(Xq, Kb, (wave * 4 + i) * 16, m0, M, k0, tX, lane);
+    for (int i = 0; i < 4; i++) {
+      if constexpr (XT) {
+        // Tiled Xq ([256-row panel][64-byte k step][256 rows][64 B], rows padded to the panel):
+        // the 16 rows of this copy are one contiguous 1 KB block.
+        const int row0 = (wave * 4 + i) * 16;
+        const int r = row0 + (lane >> 2);
+        const int c = (lane & 3) ^ swz(r);
+        const uint8_t* src = Xq + (((int64_t)tm * (Kb >> 6) + (k0 >> 6)) << 14) + (r << 6) + 16 * c;
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(tX + row0 * kBKB), 16, 0, 0);
+      } else {
+        copy_rows(Xq, Kb, (wave * 4 + i) * 16, m0, M, k0, tX, lane);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 2; i++) copy_rows(Wq, Kb, (wave * 2 + i) * 16, n0, N, k0, tW, lane);
   };
@@ -363,42 +375,51 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
   }
 }
 
-template <int BITS, int OUT>
+template <int BITS, int OUT, bool XT>
 hipError_t launch(const void* Xq, const float* sx, const void* Wq, const float* sw,
                   const float* bias, int64_t M, int64_t N, int64_t Kb, void* Y, hipStream_t st) {
   const int tiles_m = (int)((M + kBM - 1) / kBM);
   const int tiles_n = (int)((N + kBN - 1) / kBN);
   const int ntiles = tiles_m * tiles_n;
   const int grid = ((ntiles + 7) / 8) * 8;
-  hipLaunchKernelGGL((gemm_kernel<BITS, OUT>), dim3(grid), dim3(kThreads), 0, st,
+  hipLaunchKernelGGL((gemm_kernel<BITS, OUT, XT>), dim3(grid), dim3(kThreads), 0, st,
                      static_cast<const uint8_t*>(Xq), sx, static_cast<const uint8_t*>(Wq), sw,
                      bias, Y, (int)M, (int)N, (int)Kb, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
+template <bool XT>
+hipError_t launch_layout(const void* Xq, const float* sx, const void* Wq, const float* sw,
+                         const float* bias, int64_t M, int64_t N, int64_t Kb, int bits, void* Y,
+                         int out_dt, int32_t* acc32, hipStream_t stream) {
+  if (acc32) {
+    return bits == 8 ? launch<8, kOutS32, XT>(Xq, sx, Wq, sw, bias, M, N, Kb, acc32, stream)
+                     : launch<4, kOutS32, XT>(Xq, sx, Wq, sw, bias, M, N, Kb, acc32, stream);
+  }
+  if (out_dt == kF16)
+    return bits == 8 ? launch<8, kOutF16, XT>(Xq, sx, Wq, sw, bias, M, N, Kb, Y, stream)
+                     : launch<4, kOutF16, XT>(Xq, sx, Wq, sw, bias, M, N, Kb, Y, stream);
+  return bits == 8 ? launch<8, kOutBF16, XT>(Xq, sx, Wq, sw, bias, M, N, Kb, Y, stream)
+                   : launch<4, kOutBF16, XT>(Xq, sx, Wq, sw, bias, M, N, Kb, Y, stream);
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const void* Xq, const float* sx, const void* Wq, const float* sw,
-                       const float* bias, int64_t M, int64_t N, int64_t K, int bits, void* Y,
-                       int out_dt, int32_t* acc32, hipStream_t stream) {
+                       const float* bias, int64_t M, int64_t N, int64_t K, int bits,
+                       bool x_tiled, void* Y, int out_dt, int32_t* acc32, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   const int64_t Kb = bits == 8 ? K : K / 2;
-  // Kernel choice, from timings of both kernels on MI355X over the workloads' shapes: this
-  // kernel (two 256 x 128 workgroups per CU, each one's epilogue hidden behind the other's
-  // k loop) is faster or equal everywhere except long K on enough tiles to fill the machine,
-  // where the 256 x 256 kernel's lower operand traffic per MFMA wins (by up to ~20%).
+  // Tiled activation codes (the fused path): this kernel measured fastest on every workload
+  // shape. Row-major codes: it is also the default, except for long K on enough tiles to fill
+  // the machine, where the 256 x 256 kernel's lower operand traffic per MFMA measured faster
+  // (by up to ~20%) than this kernel's 64-byte row segments.
+  if (x_tiled)
+    return launch_layout<true>(Xq, sx, Wq, sw, bias, M, N, Kb, bits, Y, out_dt, acc32, stream);
   const int64_t wide_tiles = ((M + 255) / 256) * ((N + 255) / 256);
   if (wide_gemm_supported(Kb) && Kb >= 1536 && wide_tiles >= 192)
     return launch_gemm_wide(Xq, sx, Wq, sw, bias, M, N, K, bits, Y, out_dt, acc32, stream);
-  if (acc32) {
-    return bits == 8 ? launch<8, kOutS32>(Xq, sx, Wq, sw, bias, M, N, Kb, acc32, stream)
-                     : launch<4, kOutS32>(Xq, sx, Wq, sw, bias, M, N, Kb, acc32, stream);
-  }
-  if (out_dt == kF16)
-    return bits == 8 ? launch<8, kOutF16>(Xq, sx, Wq, sw, bias, M, N, Kb, Y, stream)
-                     : launch<4, kOutF16>(Xq, sx, Wq, sw, bias, M, N, Kb, Y, stream);
-  return bits == 8 ? launch<8, kOutBF16>(Xq, sx, Wq, sw, bias, M, N, Kb, Y, stream)
-                   : launch<4, kOutBF16>(Xq, sx, Wq, sw, bias, M, N, Kb, Y, stream);
+  return launch_layout<false>(Xq, sx, Wq, sw, bias, M, N, Kb, bits, Y, out_dt, acc32, stream);
 }
 
 }  // namespace convrot

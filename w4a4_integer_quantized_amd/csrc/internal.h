@@ -8,16 +8,18 @@ namespace convrot {
 
 enum InDtype { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
-// Rotate + quantize `rows` rows of length K (dtype `dt`) into codes Q (int8 [rows, K] or
-// packed int4 [rows, K/2]) and one fp32 scale per row. Arguments are pre-validated.
+// Rotate + quantize `rows` rows of length K (dtype `dt`) into codes Q (int8 or packed int4;
+// row-major, or the tiled layout of convrot.h when `tiled`) and one fp32 scale per row.
+// Arguments are pre-validated.
 hipError_t launch_rotate_quant(const void* X, int dt, int64_t rows, int64_t K, int bits,
-                               void* Q, float* S, hipStream_t stream);
+                               bool tiled, void* Q, float* S, hipStream_t stream);
 
-// acc = Xq * Wq^T over K (codes of `bits` bits), then either the dequantizing epilogue into
-// Y (out_dt kF16 / kBF16) or, when acc32 != nullptr, the raw int32 accumulators.
+// acc = Xq * Wq^T over K (codes of `bits` bits; Xq row-major or tiled when x_tiled, Wq
+// row-major), then either the dequantizing epilogue into Y (out_dt kF16 / kBF16) or, when
+// acc32 != nullptr, the raw int32 accumulators.
 hipError_t launch_gemm(const void* Xq, const float* sx, const void* Wq, const float* sw,
                        const float* bias, int64_t M, int64_t N, int64_t K, int bits,
-                       void* Y, int out_dt, int32_t* acc32, hipStream_t stream);
+                       bool x_tiled, void* Y, int out_dt, int32_t* acc32, hipStream_t stream);
 
 // The same GEMM on 256 x 256 tiles with 128-byte k steps (launch_gemm picks it for long K);
 // it needs Kb (K in bytes of codes) to be a multiple of 128 and at least 256.

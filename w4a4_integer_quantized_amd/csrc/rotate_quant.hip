@@ -105,10 +105,16 @@ __device__ __forceinline__ uint32_t code_bits(float u, float tinv) {
   return __float_as_uint(__fadd_rn(__fmul_rn(u, tinv), kRoundMagic));
 }
 
-// Quantize + store one piece (8 codes) at element offset `elem` of a row.
+// Byte offset of code byte kb (of Kb per row) of row `row`: row-major, or the tiled layout of
+// convrot.h ([256-row panel][64-byte k step][256 rows][64 B]; Kb is a multiple of 64).
+__device__ __forceinline__ int64_t code_offset(int64_t row, int64_t kb, int64_t Kb, bool tiled) {
+  if (!tiled) return row * Kb + kb;
+  return (((row >> 8) * (Kb >> 6) + (kb >> 6)) << 14) + ((row & 255) << 6) + (kb & 63);
+}
+
+// Quantize + store one piece (8 codes) at `dst` (their bytes are contiguous in both layouts).
 template <int BITS>
-__device__ __forceinline__ void store_piece(void* Q, int64_t row_elem0, int64_t elem,
-                                            const float (&v)[8], float tinv) {
+__device__ __forceinline__ void store_piece(uint8_t* dst, const float (&v)[8], float tinv) {
   uint32_t y[8];
 #pragma unroll
   for (int i = 0; i < 8; i++) y[i] = code_bits(v[i], tinv);
@@ -116,12 +122,12 @@ __device__ __forceinline__ void store_piece(void* Q, int64_t row_elem0, int64_t 
     uint2 o;
     o.x = (y[0] & 0xFFu) | ((y[1] & 0xFFu) << 8) | ((y[2] & 0xFFu) << 16) | (y[3] << 24);
     o.y = (y[4] & 0xFFu) | ((y[5] & 0xFFu) << 8) | ((y[6] & 0xFFu) << 16) | (y[7] << 24);
-    *reinterpret_cast<uint2*>(static_cast<int8_t*>(Q) + row_elem0 + elem) = o;
+    *reinterpret_cast<uint2*>(dst) = o;
   } else {
     uint32_t o = 0;
 #pragma unroll
     for (int i = 0; i < 8; i++) o |= (y[i] & 0xFu) << (4 * i);
-    *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(Q) + (row_elem0 + elem) / 2) = o;
+    *reinterpret_cast<uint32_t*>(dst) = o;
   }
 }
 
@@ -198,9 +204,10 @@ __device__ __forceinline__ uint32_t pack4_i8(uint32_t y0, uint32_t y1, uint32_t 
   return lo | hi;
 }
 
-// Quantize + store the 32 consecutive codes of v[0..3] (elements elem .. elem + 31).
+// Quantize + store the 32 consecutive codes of v[0..3] at `dst` (32 or 16 contiguous bytes in
+// both layouts: a lane's run never crosses a 64-byte k step).
 template <int BITS>
-__device__ __forceinline__ void quant_store32(void* Q, int64_t elem, const float (&v)[4][8], float tinv) {
+__device__ __forceinline__ void quant_store32(uint8_t* dst, const float (&v)[4][8], float tinv) {
   uint32_t w[8];
 #pragma unroll
   for (int i = 0; i < 4; i++) {
@@ -218,11 +225,11 @@ __device__ __forceinline__ void quant_store32(void* Q, int64_t elem, const float
     }
   }
   if constexpr (BITS == 8) {
-    uint4* p = reinterpret_cast<uint4*>(static_cast<int8_t*>(Q) + elem);
+    uint4* p = reinterpret_cast<uint4*>(dst);
     p[0] = make_uint4(w[0], w[1], w[2], w[3]);
     p[1] = make_uint4(w[4], w[5], w[6], w[7]);
   } else {
-    *reinterpret_cast<uint4*>(static_cast<uint8_t*>(Q) + elem / 2) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -231,8 +238,8 @@ __device__ __forceinline__ void quant_store32(void* Q, int64_t elem, const float
 template <int DT, int BITS, int BPQ>
 __global__ __launch_bounds__(256) void rotate_quant_kernel(const void* __restrict__ X, int64_t M,
                                                            int K, int L, int qpr,
-                                                           void* __restrict__ Q,
-                                                           float* __restrict__ S) {
+                                                           uint8_t* __restrict__ Q,
+                                                           float* __restrict__ S, int tiled) {
   __shared__ float red[4];
   const int tid = threadIdx.x;
   // L is a power of two <= 64 (256 / L rows per block) or the whole block (one row).
@@ -244,7 +251,6 @@ __global__ __launch_bounds__(256) void rotate_quant_kernel(const void* __restric
   const int q = t >> 2, tq = t & 3;
   const bool qvalid = q < qpr;
   const int qc = qvalid ? q : qpr - 1;
-  const int64_t row_elem0 = row * (int64_t)K;
   // Rows past the end and idle quads re-read valid data (never stored): no divergent path.
   const int64_t load_elem0 = (active ? row : M - 1) * (int64_t)K;
 
@@ -293,9 +299,12 @@ __global__ __launch_bounds__(256) void rotate_quant_kernel(const void* __restric
   float tinv, scale;
   row_scalars(a, qmax, tq, tinv, scale);
   if (active && qvalid) {
+    const int64_t Kb = (int64_t)K * BITS / 8;
 #pragma unroll
-    for (int be = 0; be < BPQ; be++)
-      quant_store32<BITS>(Q, row_elem0 + (int64_t)(be * qpr + q) * 128 + 32 * tq, v[be], tinv);
+    for (int be = 0; be < BPQ; be++) {
+      const int64_t kb = ((int64_t)(be * qpr + q) * 128 + 32 * tq) * BITS / 8;
+      quant_store32<BITS>(Q + code_offset(row, kb, Kb, tiled), v[be], tinv);
+    }
   }
   if (active && t == 0) S[row] = scale;
 }
@@ -306,8 +315,9 @@ __global__ __launch_bounds__(256) void rotate_quant_kernel(const void* __restric
 template <int DT, int BITS>
 __global__ __launch_bounds__(256) void rotate_quant_generic_kernel(const void* __restrict__ X,
                                                                    int64_t M, int K,
-                                                                   void* __restrict__ Q,
-                                                                   float* __restrict__ S) {
+                                                                   uint8_t* __restrict__ Q,
+                                                                   float* __restrict__ S,
+                                                                   int tiled) {
   const int tid = threadIdx.x;
   const int t = tid & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (tid >> 6);
@@ -342,7 +352,7 @@ __global__ __launch_bounds__(256) void rotate_quant_generic_kernel(const void* _
       load8<DT>(X, row_elem0 + e, v);
       fwht8(v);
       cross_stages(v, m0, m1, m2, m3);
-      store_piece<BITS>(Q, row_elem0, e, v, tinv);
+      store_piece<BITS>(Q + code_offset(row, e * BITS / 8, (int64_t)K * BITS / 8, tiled), v, tinv);
     }
   }
   if (t == 0) S[row] = scale;
@@ -355,36 +365,38 @@ struct RqShape {
 };
 
 template <int DT, int BITS, int BPQ>
-hipError_t launch_fast(const void* X, int64_t M, int K, RqShape sh, void* Q, float* S, hipStream_t st) {
+hipError_t launch_fast(const void* X, int64_t M, int K, RqShape sh, uint8_t* Q, float* S, int tiled,
+                       hipStream_t st) {
   const int threads = sh.L <= 64 ? 256 : sh.L;
   const int rows_per_block = threads / sh.L;
   const int64_t blocks = (M + rows_per_block - 1) / rows_per_block;
   hipLaunchKernelGGL((rotate_quant_kernel<DT, BITS, BPQ>), dim3((unsigned)blocks), dim3(threads), 0,
-                     st, X, M, K, sh.L, sh.qpr, Q, S);
+                     st, X, M, K, sh.L, sh.qpr, Q, S, tiled);
   return hipGetLastError();
 }
 
 template <int DT, int BITS>
-hipError_t launch_bits(const void* X, int64_t M, int K, RqShape sh, void* Q, float* S, hipStream_t st) {
+hipError_t launch_bits(const void* X, int64_t M, int K, RqShape sh, uint8_t* Q, float* S, int tiled,
+                       hipStream_t st) {
   switch (sh.bpq) {
-    case 1: return launch_fast<DT, BITS, 1>(X, M, K, sh, Q, S, st);
-    case 2: return launch_fast<DT, BITS, 2>(X, M, K, sh, Q, S, st);
-    case 3: return launch_fast<DT, BITS, 3>(X, M, K, sh, Q, S, st);
-    case 4: return launch_fast<DT, BITS, 4>(X, M, K, sh, Q, S, st);
+    case 1: return launch_fast<DT, BITS, 1>(X, M, K, sh, Q, S, tiled, st);
+    case 2: return launch_fast<DT, BITS, 2>(X, M, K, sh, Q, S, tiled, st);
+    case 3: return launch_fast<DT, BITS, 3>(X, M, K, sh, Q, S, tiled, st);
+    case 4: return launch_fast<DT, BITS, 4>(X, M, K, sh, Q, S, tiled, st);
     default: {
       const int64_t blocks = (M + 3) / 4;
       hipLaunchKernelGGL((rotate_quant_generic_kernel<DT, BITS>), dim3((unsigned)blocks),
-                         dim3(256), 0, st, X, M, K, Q, S);
+                         dim3(256), 0, st, X, M, K, Q, S, tiled);
       return hipGetLastError();
     }
   }
 }
 
 template <int DT>
-hipError_t launch_dt(const void* X, int64_t M, int K, int bits, RqShape sh, void* Q, float* S,
-                     hipStream_t st) {
-  return bits == 8 ? launch_bits<DT, 8>(X, M, K, sh, Q, S, st)
-                   : launch_bits<DT, 4>(X, M, K, sh, Q, S, st);
+hipError_t launch_dt(const void* X, int64_t M, int K, int bits, RqShape sh, uint8_t* Q, float* S,
+                     int tiled, hipStream_t st) {
+  return bits == 8 ? launch_bits<DT, 8>(X, M, K, sh, Q, S, tiled, st)
+                   : launch_bits<DT, 4>(X, M, K, sh, Q, S, tiled, st);
 }
 
 }  // namespace
@@ -407,14 +419,16 @@ RqShape choose_rotate_quant_shape(int64_t K) {
   return {0, 0, 64};
 }
 
-hipError_t launch_rotate_quant(const void* X, int dt, int64_t rows, int64_t K, int bits, void* Q,
-                               float* S, hipStream_t stream) {
+hipError_t launch_rotate_quant(const void* X, int dt, int64_t rows, int64_t K, int bits, bool tiled,
+                               void* Q, float* S, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   const RqShape sh = choose_rotate_quant_shape(K);
+  uint8_t* q = static_cast<uint8_t*>(Q);
+  const int t = tiled ? 1 : 0;
   switch (dt) {
-    case kF32: return launch_dt<kF32>(X, rows, (int)K, bits, sh, Q, S, stream);
-    case kF16: return launch_dt<kF16>(X, rows, (int)K, bits, sh, Q, S, stream);
-    default: return launch_dt<kBF16>(X, rows, (int)K, bits, sh, Q, S, stream);
+    case kF32: return launch_dt<kF32>(X, rows, (int)K, bits, sh, q, S, t, stream);
+    case kF16: return launch_dt<kF16>(X, rows, (int)K, bits, sh, q, S, t, stream);
+    default: return launch_dt<kBF16>(X, rows, (int)K, bits, sh, q, S, t, stream);
   }
 }
 
