@@ -55,6 +55,12 @@ def _load():
         lib.orc_hadamard_entry.argtypes = [I, I]
         lib.orc_hadamard_entry.restype = I
         lib.orc_num_threads.restype = I
+        lib.orc_quantize_rows_mse.argtypes = [P, I, I64, I64, I, P, P, P, P]
+        lib.orc_quantize_rows_mse.restype = I
+        lib.orc_quantize_tensorwise.argtypes = [P, I, I64, I64, I, P, P, P]
+        lib.orc_quantize_tensorwise.restype = I
+        lib.orc_clip_alpha.argtypes = [I]
+        lib.orc_clip_alpha.restype = ctypes.c_float
         _lib = lib
     return _lib
 
@@ -152,6 +158,57 @@ def quantize_rows(x: np.ndarray, dtype: int, bits: int = 8, rotate: bool = True,
                                    _ptr(pre) if pre is not None else None)
     if rc != 0:
         raise RuntimeError("oracle quantize_rows failed (%d)" % rc)
+    return codes, scales, pre
+
+
+NCLIP = 51   # clipping candidates alpha_i = fl((100 - i) / 100), i = 0..50
+
+
+def clip_alpha(i: int) -> np.float32:
+    return np.float32(_load().orc_clip_alpha(i))
+
+
+def _check_rows_input(x, dtype):
+    x = np.ascontiguousarray(x)
+    assert x.ndim == 2
+    if dtype == F32:
+        assert x.dtype == np.float32
+    else:
+        assert x.dtype == np.uint16
+    return x
+
+
+def quantize_rows_mse(x: np.ndarray, dtype: int, bits: int = 8):
+    """Rotate, then per-row MSE-optimized clipping (the release page's recipe, step 3).
+
+    Returns (codes int8 [rows, K], scales float32 [rows], alpha_idx int32 [rows],
+    err float64 [rows, NCLIP] -- every candidate's squared reconstruction error)."""
+    x = _check_rows_input(x, dtype)
+    rows, K = x.shape
+    codes = np.empty((rows, K), np.int8)
+    scales = np.empty((rows,), np.float32)
+    idx = np.empty((rows,), np.int32)
+    err = np.empty((rows, NCLIP), np.float64)
+    rc = _load().orc_quantize_rows_mse(_ptr(x), dtype, rows, K, bits, _ptr(codes), _ptr(scales),
+                                       _ptr(idx), _ptr(err))
+    if rc != 0:
+        raise RuntimeError("oracle quantize_rows_mse failed (%d)" % rc)
+    return codes, scales, idx, err
+
+
+def quantize_tensorwise(x: np.ndarray, dtype: int, bits: int = 8, want_pre: bool = False):
+    """Rotate, then one absmax scale for the whole tensor (every row gets the same scale).
+
+    Returns (codes int8 [rows, K], scales float32 [rows], pre float32 [rows, K] or None)."""
+    x = _check_rows_input(x, dtype)
+    rows, K = x.shape
+    codes = np.empty((rows, K), np.int8)
+    scales = np.empty((rows,), np.float32)
+    pre = np.empty((rows, K), np.float32) if want_pre else None
+    rc = _load().orc_quantize_tensorwise(_ptr(x), dtype, rows, K, bits, _ptr(codes), _ptr(scales),
+                                         _ptr(pre) if pre is not None else None)
+    if rc != 0:
+        raise RuntimeError("oracle quantize_tensorwise failed (%d)" % rc)
     return codes, scales, pre
 
 

@@ -196,6 +196,116 @@ int orc_quantize_rows(const void *x, int dtype, int64_t rows, int64_t K, int bit
   return bad ? -1 : 0;
 }
 
+/* ------------------------------------------------------------------------------------ */
+/* Weight-quantizer variants.                                                           */
+/* ------------------------------------------------------------------------------------ */
+
+#define ORC_NCLIP 51   /* clipping candidates alpha = 1.00, 0.99, ..., 0.50 */
+
+/* Candidate i's clipping factor: the binary32 nearest to (100 - i) / 100. */
+float orc_clip_alpha(int i) { return (float)(100 - i) / 100.0f; }
+
+/* Quantize the rotated row u[K] against clipping threshold t (> 0): inv = fl(q_max / t),
+ * s = fl(fl(t * c) / q_max), q_k = clamp(rne(fl(u_k * inv)), -q_max, q_max). Returns s and, in
+ * err, sum_k (u_k * c - s * q_k)^2 evaluated in binary64 in increasing k (the products are
+ * exact in binary64; the differences, squares and sums are rounded). */
+static float quantize_clipped(const float *u, int64_t K, float t, float qmax, float c, int8_t *q,
+                              double *err) {
+  const float inv = qmax / t;
+  const float s = (t * c) / qmax;
+  double e = 0.0;
+  for (int64_t k = 0; k < K; k++) {
+    float v = nearbyintf(u[k] * inv);
+    if (v > qmax) v = qmax;
+    if (v < -qmax) v = -qmax;
+    q[k] = (int8_t)v;
+    const double d = (double)u[k] * (double)c - (double)s * (double)v;
+    e += d * d;
+  }
+  *err = e;
+  return s;
+}
+
+/* MSE-optimized clipping (the release page's "Quantization recipe", step 3, with the reading
+ * stated in the design notes): per row, after the rotation, the clipping threshold
+ * t = fl(a * alpha_i) is chosen among the ORC_NCLIP candidates to minimize the squared
+ * reconstruction error of the normalized rotated row (quantize_clipped); ties keep the larger
+ * alpha. alpha = 1 reproduces orc_quantize_rows. A zero row gets scale 0 and codes 0.
+ * alpha_idx [rows] (or NULL) receives the chosen candidate, err [rows * ORC_NCLIP] (or NULL)
+ * every candidate's error. Rotation always on. */
+int orc_quantize_rows_mse(const void *x, int dtype, int64_t rows, int64_t K, int bits,
+                          int8_t *codes, float *scales, int32_t *alpha_idx, double *err) {
+  if (K <= 0 || K % ORC_BLOCK != 0 || (bits != 8 && bits != 4) || rows < 0) return -2;
+  const float qmax = (bits == 8) ? 127.0f : 7.0f;
+  const float c = orc_inv_sqrt_block();
+#pragma omp parallel for schedule(dynamic)
+  for (int64_t r = 0; r < rows; r++) {
+    float *u = (float *)malloc((size_t)K * sizeof(float));
+    int8_t *q = (int8_t *)malloc((size_t)K);
+    for (int64_t k = 0; k < K; k++) u[k] = load_elem(x, dtype, r * K + k);
+    for (int64_t b = 0; b < K / ORC_BLOCK; b++) orc_fwht128(u + b * ORC_BLOCK);
+    float a = 0.0f;
+    for (int64_t k = 0; k < K; k++) a = fmaxf(a, fabsf(u[k]));
+    if (a == 0.0f) {
+      scales[r] = 0.0f;
+      memset(codes + r * K, 0, (size_t)K);
+      if (alpha_idx) alpha_idx[r] = 0;
+      if (err)
+        for (int i = 0; i < ORC_NCLIP; i++) err[r * ORC_NCLIP + i] = 0.0;
+    } else {
+      int best = 0;
+      double best_e = 0.0;
+      for (int i = 0; i < ORC_NCLIP; i++) {
+        double e;
+        quantize_clipped(u, K, a * orc_clip_alpha(i), qmax, c, q, &e);
+        if (err) err[r * ORC_NCLIP + i] = e;
+        if (i == 0 || e < best_e) {
+          best = i;
+          best_e = e;
+        }
+      }
+      double e;
+      scales[r] = quantize_clipped(u, K, a * orc_clip_alpha(best), qmax, c, codes + r * K, &e);
+      if (alpha_idx) alpha_idx[r] = best;
+    }
+    free(q);
+    free(u);
+  }
+  return 0;
+}
+
+/* Tensor-wise scale (the HSWQ model card's int8_tensorwise variant, here after the same
+ * rotation): one absmax A over the whole rotated tensor; every row is quantized with
+ * inv = fl(q_max / A) and gets the same scale fl(fl(A * c) / q_max). A zero tensor gets scales
+ * 0 and codes 0. pre (or NULL) receives fl(u * inv). Rotation always on. */
+int orc_quantize_tensorwise(const void *x, int dtype, int64_t rows, int64_t K, int bits,
+                            int8_t *codes, float *scales, float *pre) {
+  if (K <= 0 || K % ORC_BLOCK != 0 || (bits != 8 && bits != 4) || rows < 0) return -2;
+  const float qmax = (bits == 8) ? 127.0f : 7.0f;
+  const float c = orc_inv_sqrt_block();
+  float *u = (float *)malloc((size_t)(rows * K > 0 ? rows * K : 1) * sizeof(float));
+  float A = 0.0f;
+#pragma omp parallel for schedule(static) reduction(max : A)
+  for (int64_t r = 0; r < rows; r++) {
+    float *ur = u + r * K;
+    for (int64_t k = 0; k < K; k++) ur[k] = load_elem(x, dtype, r * K + k);
+    for (int64_t b = 0; b < K / ORC_BLOCK; b++) orc_fwht128(ur + b * ORC_BLOCK);
+    for (int64_t k = 0; k < K; k++) A = fmaxf(A, fabsf(ur[k]));
+  }
+  const float inv = (A > 0.0f) ? qmax / A : 0.0f;
+  const float s = (A * c) / qmax;
+  for (int64_t r = 0; r < rows; r++) {
+    scales[r] = (A > 0.0f) ? s : 0.0f;
+    for (int64_t k = 0; k < K; k++) {
+      const float p = u[r * K + k] * inv;
+      codes[r * K + k] = (int8_t)nearbyintf(p);
+      if (pre) pre[r * K + k] = p;
+    }
+  }
+  free(u);
+  return 0;
+}
+
 /* int4 packing: byte[r, j] = (q[r, 2j] & 0xF) | ((q[r, 2j+1] & 0xF) << 4), i.e. two's
  * complement nibbles, low nibble = even k. */
 void orc_pack_int4(const int8_t *codes, int64_t rows, int64_t K, uint8_t *packed) {
