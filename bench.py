@@ -34,6 +34,8 @@ sys.path.insert(0, ROOT)
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, TOP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
 MALL_BYTES = 256 << 20
+PEAK_F64_OPS = 39.3e12       # MI355X vector fp64, non-fused ops/s (78.6 TFLOP/s counts an FMA as 2)
+NCLIP = 51                   # clipping candidates of the MSE weight-scale rule
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 
 
@@ -191,6 +193,51 @@ def cpu_baseline(g, cfg, target_s):
             "kind": "oracle",
             "sample": "first %d of %d tokens, every linear of the step (rotate+quantize, int GEMM, "
                       "epilogue), %d passes, %.1f s" % (rows, cfg.M, passes, total_t)}
+
+
+def offline_weight_quant(rq, torch, W_np, bits, dev, reps=5):
+    """Times rq_quantize_weights under each weight-scale rule on one weight matrix, with the
+    weight quantization error of each rule (row sample, against the exact rotation in float64:
+    plain numpy block-Hadamard, W_rot = W blockdiag(H_128) / sqrt(128))."""
+    import numpy as np
+    import scipy.linalg
+    N, K = W_np.shape
+    Wd = torch.from_numpy(W_np).to(dev)
+    rows = np.random.default_rng(7).choice(N, min(N, 256), replace=False)
+    Hn = scipy.linalg.hadamard(128).astype(np.float64) / math.sqrt(128.0)
+    wr = W_np[rows].astype(np.float64).reshape(len(rows), K // 128, 128) @ Hn
+    wr = wr.reshape(len(rows), K)
+    out = {"N": N, "K": K, "bits": bits, "w_dtype": "f32"}
+    alg_bytes = 4 * N * K + N * K * bits // 8 + 4 * N
+    for name, mode in (("absmax", rq.RQ_W_ABSMAX), ("mse", rq.RQ_W_MSE), ("tensor", rq.RQ_W_TENSOR)):
+        rq.quantize_weights(Wd, bits=bits, w_scale_mode=mode)     # warm-up
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            Wq, ws = rq.quantize_weights(Wd, bits=bits, w_scale_mode=mode)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = float(np.median(ts))
+        codes = Wq.cpu().numpy()
+        if bits == 4:
+            lo = (codes.view(np.uint8) & 0xF).astype(np.int8)
+            hi = (codes.view(np.uint8) >> 4).astype(np.int8)
+            lo[lo >= 8] -= 16
+            hi[hi >= 8] -= 16
+            codes = np.stack([lo, hi], axis=-1).reshape(N, K)
+        deq = codes[rows].astype(np.float64) * ws.cpu().numpy()[rows, None].astype(np.float64)
+        d = {"ms": round(ms, 4), "GBps": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
+             "w_err_rel_frobenius": round(float(np.linalg.norm(deq - wr) / np.linalg.norm(wr)), 6)}
+        if mode == rq.RQ_W_MSE:
+            # Each candidate evaluation is 5 binary64 operations by definition (two exact
+            # products, a difference, a square, a sum); the search evaluates NCLIP * N * K.
+            f64 = 5.0 * NCLIP * N * K / (ms * 1e-3)
+            d["roofline"] = {"bound": "alu", "achieved": round(f64 / 1e12, 2), "peak": PEAK_F64_OPS / 1e12,
+                             "unit": "T fp64 op/s", "frac": round(f64 / PEAK_F64_OPS, 4)}
+        out[name] = d
+    return out
 
 
 def synth_workload_name(key):
@@ -400,6 +447,8 @@ def main():
         "weight_quant_ms_offline": round(wq_ms, 3), "buffer_sets": R,
         "quant_error_rel_frobenius_vs_fp64": qerr,
     }
+    log("offline weight quantizer rules on %s" % dom.name)
+    out["weight_quantizer"] = offline_weight_quant(rq, torch, g["W"][dom.name], bits, dev)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle, ~%.0f s)" % args.cpu_seconds)
         out["cpu_baseline"] = cpu_baseline(g, cfg, args.cpu_seconds)

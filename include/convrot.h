@@ -70,6 +70,22 @@ enum { RQ_ROT_WHT = 1 };   /* normalized Walsh-Hadamard rotation, Sylvester orde
 
 enum { RQ_X_ROWS = 0, RQ_X_TILED = 1 };   /* activation code layouts (see above) */
 
+/* Weight-scale rules of rq_quantize_weights. Each picks a clipping threshold t per row and
+ * then quantizes exactly as above with a replaced by t: inv = fl(q_max / t),
+ * scale = fl(fl(t * fl(1/sqrt 128)) / q_max), code = clamp(round_half_even(fl(u * inv)),
+ * -q_max, q_max); t = 0 gives scale 0 and codes 0.
+ *   RQ_W_ABSMAX   t = a = max |u| of the row (the default; the rule of the activations).
+ *   RQ_W_MSE      MSE-optimized clipping ("Quantization recipe", step 3: the converter picks
+ *                 the clipping scale with the least squared error). t = fl(a * alpha_i),
+ *                 alpha_i = fl((100 - i) / 100), i = 0..50, minimizing
+ *                 E_i = sum_k (u_k * fl(1/sqrt 128) - scale_i * code_ik)^2, evaluated in
+ *                 binary64 in increasing k (the two products exact, the difference, square and
+ *                 running sum each rounded to nearest); ties keep the smaller i (larger alpha).
+ *   RQ_W_TENSOR   tensor-wise scale (the int8_tensorwise variant of the HSWQ ConvRot model
+ *                 card): t = max |u| over the whole rotated matrix, so every row gets the same
+ *                 scale. The GEMM is unchanged: w_scale[n] is simply constant. */
+enum { RQ_W_ABSMAX = 0, RQ_W_MSE = 1, RQ_W_TENSOR = 2 };
+
 typedef struct {
   int32_t bits;       /* 8 (W8A8) or 4 (W4A4) */
   int32_t rot_kind;   /* must be RQ_ROT_WHT */
@@ -77,6 +93,8 @@ typedef struct {
   int32_t x_layout;   /* RQ_X_ROWS or RQ_X_TILED: layout of Xq in rq_rotate_quantize,
                          rq_gemm_dequant and rq_gemm_s32 (rq_quantize_weights ignores it;
                          rq_rotq_linear always uses RQ_X_TILED inside its workspace) */
+  int32_t w_scale_mode; /* RQ_W_ABSMAX, RQ_W_MSE or RQ_W_TENSOR: the scale rule of
+                           rq_quantize_weights (every other entry point ignores it) */
 } rq_qconfig;
 
 /* Bytes of activation codes for `rows` rows of length K in cfg's bits and x_layout
@@ -84,10 +102,10 @@ typedef struct {
 size_t rq_codes_bytes(int64_t rows, int64_t K, const rq_qconfig *cfg);
 
 /* Offline weight quantizer ("Quantization recipe": upcast to FP32, block-Hadamard transform,
- * per-row scales).
+ * per-row scales), with the scale rule cfg->w_scale_mode.
  *   W        [N, K] device, dtype w_dtype (RQ_F32, RQ_F16 or RQ_BF16)
  *   Wq       out: int8 [N, K] (bits 8) or uint8 [N, K/2] (bits 4)
- *   w_scale  out: float [N]
+ *   w_scale  out: float [N] (RQ_W_TENSOR also uses it as scratch between its kernels)
  * Returns RQ_OK or a status; see the conventions above. */
 rq_status rq_quantize_weights(const void *W, int32_t w_dtype, int64_t N, int64_t K,
                               const rq_qconfig *cfg, void *Wq, float *w_scale, void *stream);

@@ -130,6 +130,14 @@ def test_entry_points_reject_before_launch():
     # M == 0 is a no-op that succeeds without launching anything
     assert rq.rq_gemm_s32(A, A + GB, 0, 32, 128, cfg, A + 2 * GB, None) == rq.RQ_OK
     assert rq.rq_rotate_quantize(A, rq.RQ_F16, 0, 128, cfg, A + GB, A + 2 * GB, None) == rq.RQ_OK
+    # The weight-scale rule is validated for every entry point; N == 0 is a no-op in each rule.
+    bad = rq.make_cfg(8, w_scale_mode=3)
+    assert rq.rq_quantize_weights(A, rq.RQ_F32, 16, 128, bad, A + GB, A + 2 * GB, None) == rq.RQ_EINVAL
+    assert rq.rq_gemm_s32(A, A + GB, 16, 32, 128, bad, A + 2 * GB, None) == rq.RQ_EINVAL
+    for mode in (rq.RQ_W_ABSMAX, rq.RQ_W_MSE, rq.RQ_W_TENSOR):
+        c = rq.make_cfg(4, w_scale_mode=mode)
+        assert rq.rq_quantize_weights(A, rq.RQ_F32, 0, 256, c, A + GB, A + 2 * GB, None) == rq.RQ_OK
+        assert rq.rq_quantize_weights(A, rq.RQ_F32, 16, 200, c, A + GB, A + 2 * GB, None) == rq.RQ_EUNSUPPORTED
 
 
 def test_tensor_wrappers_refuse_host_tensors():

@@ -23,6 +23,7 @@ RQ_OK, RQ_EINVAL, RQ_EUNSUPPORTED, RQ_EWORKSPACE, RQ_EHIP = range(5)
 RQ_F32, RQ_F16, RQ_BF16 = 0, 1, 2
 RQ_ROT_WHT = 1
 RQ_X_ROWS, RQ_X_TILED = 0, 1
+RQ_W_ABSMAX, RQ_W_MSE, RQ_W_TENSOR = 0, 1, 2
 
 
 class ConvRotError(RuntimeError):
@@ -33,7 +34,7 @@ class ConvRotError(RuntimeError):
 
 class rq_qconfig(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int32), ("rot_kind", ctypes.c_int32), ("rot_block", ctypes.c_int32),
-                ("x_layout", ctypes.c_int32)]
+                ("x_layout", ctypes.c_int32), ("w_scale_mode", ctypes.c_int32)]
 
 
 _lib = None
@@ -94,8 +95,8 @@ def _check(status: int, where: str):
 
 
 def make_cfg(bits: int = 8, rot_block: int = 128, rot_kind: int = RQ_ROT_WHT,
-             x_layout: int = RQ_X_ROWS) -> rq_qconfig:
-    return rq_qconfig(bits, rot_kind, rot_block, x_layout)
+             x_layout: int = RQ_X_ROWS, w_scale_mode: int = RQ_W_ABSMAX) -> rq_qconfig:
+    return rq_qconfig(bits, rot_kind, rot_block, x_layout, w_scale_mode)
 
 
 # ----------------------------------------------------------------------------- raw entry points
@@ -177,13 +178,16 @@ def workspace_size(M: int, K: int, bits: int = 8) -> int:
     return rq_rotq_linear_workspace_size(M, K, make_cfg(bits))
 
 
-def quantize_weights(W, bits: int = 8, rot: int = 128, stream=None):
-    """Offline: W [N, K] (f32/f16/bf16, device) -> (Wq int8 [N, K] | uint8 [N, K/2], w_scale f32 [N])."""
+def quantize_weights(W, bits: int = 8, rot: int = 128, stream=None, w_scale_mode: int = RQ_W_ABSMAX):
+    """Offline: W [N, K] (f32/f16/bf16, device) -> (Wq int8 [N, K] | uint8 [N, K/2], w_scale f32 [N]).
+    w_scale_mode: RQ_W_ABSMAX (per-row absmax), RQ_W_MSE (per-row MSE-optimized clipping) or
+    RQ_W_TENSOR (one tensor-wise scale)."""
     torch = _torch()
     N, K = W.shape
     Wq = torch.empty(code_shape(N, K, bits), dtype=torch.int8 if bits == 8 else torch.uint8, device=W.device)
     ws = torch.empty((N,), dtype=torch.float32, device=W.device)
-    _check(rq_quantize_weights(_dev(W, "W"), _dtype_code(W), N, K, make_cfg(bits, rot),
+    _check(rq_quantize_weights(_dev(W, "W"), _dtype_code(W), N, K,
+                               make_cfg(bits, rot, w_scale_mode=w_scale_mode),
                                Wq.data_ptr(), ws.data_ptr(), _stream(stream)), "rq_quantize_weights")
     return Wq, ws
 

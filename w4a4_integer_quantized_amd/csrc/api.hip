@@ -63,6 +63,10 @@ rq_status check_cfg(const rq_qconfig* cfg) {
     return fail(RQ_EUNSUPPORTED, "rot_block = %d (supported: 128)", cfg->rot_block);
   if (cfg->x_layout != RQ_X_ROWS && cfg->x_layout != RQ_X_TILED)
     return fail(RQ_EINVAL, "x_layout = %d (RQ_X_ROWS or RQ_X_TILED)", cfg->x_layout);
+  if (cfg->w_scale_mode != RQ_W_ABSMAX && cfg->w_scale_mode != RQ_W_MSE &&
+      cfg->w_scale_mode != RQ_W_TENSOR)
+    return fail(RQ_EINVAL, "w_scale_mode = %d (RQ_W_ABSMAX, RQ_W_MSE or RQ_W_TENSOR)",
+                cfg->w_scale_mode);
   return ok();
 }
 
@@ -197,6 +201,12 @@ rq_status rq_quantize_weights(const void* W, int32_t w_dtype, int64_t N, int64_t
                               const rq_qconfig* cfg, void* Wq, float* w_scale, void* stream) {
   rq_status s = check_rotate_args(W, w_dtype, N, K, cfg, Wq, w_scale, "W", false);
   if (s) return s;
+  if (cfg->w_scale_mode != RQ_W_ABSMAX)
+    return from_hip(convrot::launch_weight_quant(cfg->w_scale_mode == RQ_W_MSE ? convrot::kWScaleMse
+                                                                                : convrot::kWScaleTensor,
+                                                 W, w_dtype, N, K, cfg->bits, Wq, w_scale,
+                                                 static_cast<hipStream_t>(stream)),
+                    "weight_quant launch");
   return from_hip(convrot::launch_rotate_quant(W, w_dtype, N, K, cfg->bits, false, Wq, w_scale,
                                                static_cast<hipStream_t>(stream)),
                   "rotate_quant launch");

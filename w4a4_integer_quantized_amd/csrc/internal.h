@@ -8,11 +8,20 @@ namespace convrot {
 
 enum InDtype { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
+// Weight-scale rules (values of rq_qconfig.w_scale_mode).
+enum WScaleMode { kWScaleAbsmax = 0, kWScaleMse = 1, kWScaleTensor = 2 };
+
 // Rotate + quantize `rows` rows of length K (dtype `dt`) into codes Q (int8 or packed int4;
 // row-major, or the tiled layout of convrot.h when `tiled`) and one fp32 scale per row.
 // Arguments are pre-validated.
 hipError_t launch_rotate_quant(const void* X, int dt, int64_t rows, int64_t K, int bits,
                                bool tiled, void* Q, float* S, hipStream_t stream);
+
+// The weight quantizer's MSE-clipped (kWScaleMse) or tensor-wise (kWScaleTensor) scale rule:
+// codes Wq (row-major int8 / packed int4) and one fp32 scale per row. Arguments are
+// pre-validated; N < 2^31.
+hipError_t launch_weight_quant(int mode, const void* W, int dt, int64_t N, int64_t K, int bits,
+                               void* Wq, float* S, hipStream_t stream);
 
 // acc = Xq * Wq^T over K (codes of `bits` bits; Xq row-major or tiled when x_tiled, Wq
 // row-major), then either the dequantizing epilogue into Y (out_dt kF16 / kBF16) or, when
