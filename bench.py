@@ -89,8 +89,42 @@ def _read_counter_csv(path):
     with open(path) as fh:
         for r in csv.DictReader(fh):
             d = out.setdefault(int(r["Dispatch_Id"]), [r["Kernel_Name"], int(r["Grid_Size"]), {}])
-            d[2][r["Counter_Name"]] = float(r["Counter_Value"])
+            # A counter reported per hardware instance arrives as several rows: sum them.
+            d[2][r["Counter_Name"]] = d[2].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
     return out
+
+
+def mfma_summary(counter_csv, trace_csv, n_simd=1024, n_xcc=8):
+    """Reduce a rocprofv3 run with --pmc MfmaUtil SQ_VALU_MFMA_BUSY_CYCLES
+    SQ_INSTS_VALU_MFMA_MOPS_I8 GRBM_GUI_ACTIVE --kernel-trace to per-launch figures of the GEMM's
+    largest launch: MFMA busy fraction, int8 MFMA ops, GPU-active cycles per XCD and the shader
+    clock they imply over the traced duration."""
+    import csv
+    import numpy as np
+    dur = {}
+    with open(trace_csv) as fh:
+        for r in csv.DictReader(fh):
+            dur[int(r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    rows = {}
+    for did, (name, grid, vals) in _read_counter_csv(counter_csv).items():
+        if "gemm_kernel" in name and did in dur:
+            rows.setdefault(grid, []).append((name, vals, dur[did]))
+    grid = max(rows)
+    name = rows[grid][0][0]
+    util = [v.get("MfmaUtil", float("nan")) for _, v, _ in rows[grid]]
+    busy = [v.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")) for _, v, _ in rows[grid]]
+    mops = [v.get("SQ_INSTS_VALU_MFMA_MOPS_I8", float("nan")) for _, v, _ in rows[grid]]
+    gui = [v.get("GRBM_GUI_ACTIVE", float("nan")) / n_xcc for _, v, _ in rows[grid]]
+    secs = [d for _, _, d in rows[grid]]
+    doc = {"kernel": name, "grid_threads": grid, "dispatches": len(secs),
+           "duration_us_median": round(float(np.median(secs)) * 1e6, 2),
+           "MfmaUtil_pct_median": round(float(np.median(util)), 2),
+           "mfma_busy_cycles_per_simd_median": round(float(np.median(busy)) / n_simd, 1),
+           "gui_active_cycles_per_xcd_median": round(float(np.median(gui)), 1),
+           "implied_clock_GHz": round(float(np.median(gui)) / float(np.median(secs)) / 1e9, 3),
+           "int8_mfma_ops_median": float(np.median(mops)) * 512}
+    print(json.dumps(doc))
+    return doc
 
 
 def _median_by_group(csv_path, counter, select):
@@ -165,13 +199,25 @@ def cpu_baseline(g, cfg, target_s):
     dt = oracle.F16 if cfg.io == "f16" else oracle.BF16
     wq = {lin.name: oracle.quantize_weights(g["W"][lin.name], cfg.bits)[0::2] for lin in cfg.linears}
 
+    split = {"rq_s": 0.0, "rq_bytes": 0, "gemm_s": 0.0, "gemm_ops": 0}
+
     def run(rows):
+        # The oracle's linear, step by step: rotate+quantize, integer GEMM, epilogue.
         t0 = time.perf_counter()
         ops = 0
         for lin in cfg.linears:
-            src = g["x_bits"] if lin.source == "x" else g["x2_bits"][lin.name]
+            src = np.ascontiguousarray((g["x_bits"] if lin.source == "x" else g["x2_bits"][lin.name])[:rows])
             wc, ws = wq[lin.name]
-            oracle.rotq_linear(np.ascontiguousarray(src[:rows]), dt, wc, ws, g["bias"][lin.name], cfg.bits)
+            t1 = time.perf_counter()
+            xc, xs, _ = oracle.quantize_rows(src, dt, cfg.bits)
+            t2 = time.perf_counter()
+            acc = oracle.gemm_s32(xc, wc)
+            oracle.epilogue(acc, xs, ws, g["bias"][lin.name], dt)
+            t3 = time.perf_counter()
+            split["rq_s"] += t2 - t1
+            split["rq_bytes"] += rows * lin.K * 2 + rows * lin.K * cfg.bits // 8 + 4 * rows
+            split["gemm_s"] += t3 - t2
+            split["gemm_ops"] += 2 * rows * lin.N * lin.K
             ops += 2 * rows * lin.N * lin.K
         return time.perf_counter() - t0, ops
 
@@ -191,6 +237,8 @@ def cpu_baseline(g, cfg, target_s):
         passes += 1
     return {"value": total_ops / total_t / 1e12, "unit": "TOPS", "cores": oracle.num_threads(),
             "kind": "oracle",
+            "rotate_quant_GBps": round(split["rq_bytes"] / split["rq_s"] / 1e9, 3),
+            "gemm_epilogue_TOPS": round(split["gemm_ops"] / split["gemm_s"] / 1e12, 5),
             "sample": "first %d of %d tokens, every linear of the step (rotate+quantize, int GEMM, "
                       "epilogue), %d passes, %.1f s" % (rows, cfg.M, passes, total_t)}
 
@@ -240,6 +288,48 @@ def offline_weight_quant(rq, torch, W_np, bits, dev, reps=5):
     return out
 
 
+def library_int8_gemm(torch, M, N, K, reps=20):
+    """Context only: the vendor library's int8 GEMM (hipBLASLt through torch._int_mm) on the
+    dominant call's shape. It writes int32 (4 B per output, twice this path's fp16/bf16 Y) and
+    applies no scales or bias; it is a sanity point, not a target."""
+    A = torch.randint(-127, 128, (M, K), dtype=torch.int8, device="cuda")
+    Bt = torch.randint(-127, 128, (N, K), dtype=torch.int8, device="cuda").t()
+    for _ in range(3):
+        torch._int_mm(A, Bt)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch._int_mm(A, Bt)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    return {"shape": [M, N, K], "us": round(us, 2), "TOPS": round(2 * M * N * K / us / 1e6, 1),
+            "out": "int32, no epilogue", "via": "torch._int_mm (hipBLASLt)"}
+
+
+def gpu_state():
+    """rocm-smi's view of clocks and power right after the timed work (context)."""
+    import shutil
+    import subprocess
+    if any(k.startswith("ROCPROF") for k in os.environ):
+        return {"skipped": "running under a profiler"}
+    tool = shutil.which("rocm-smi")
+    if tool is None:
+        return {"error": "rocm-smi not found"}
+    try:
+        # The tool is a Python script: run it with this interpreter as a plain child process.
+        r = subprocess.run([sys.executable, tool, "--showclocks", "--showpower", "--json"],
+                           capture_output=True, text=True, timeout=20)
+        doc = json.loads(r.stdout) if r.returncode == 0 else {}
+    except Exception as ex:  # the tool may be absent or print no JSON
+        return {"error": str(ex)[:200]}
+    out = {}
+    for card, d in doc.items():
+        out[card] = {k: v for k, v in d.items() if any(t in k.lower() for t in ("sclk", "mclk", "fclk", "power"))}
+    return out
+
+
 def synth_workload_name(key):
     from w4a4_integer_quantized_amd import synth
     return synth.CONFIGS[key].workload
@@ -248,16 +338,21 @@ def synth_workload_name(key):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="vit_attn")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--mfma-summary", nargs=2, metavar=("COUNTER_CSV", "KERNEL_TRACE_CSV"),
+                    help="reduce a rocprofv3 MFMA-utilization run of the GEMM and exit")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="reduce rocprofv3 counter CSVs into profiles/pmc_traffic.json (no GPU)")
     args = ap.parse_args()
+    if args.mfma_summary:
+        mfma_summary(*args.mfma_summary)
+        return
     if args.pmc_summary:
         pmc_summary(synth_workload_name(args.workload), *args.pmc_summary)
         return
@@ -280,7 +375,10 @@ def main():
     g = synth.generate(args.workload)
     tdt = torch.float16 if cfg.io == "f16" else torch.bfloat16
     dev = torch.device("cuda:0")
-    stream = torch.cuda.current_stream()
+    # All work goes to one dedicated stream (default priority). Dependent kernels on the legacy
+    # null stream measured ~10% slower per step here (extra synchronization between launches).
+    stream = torch.cuda.Stream(device=dev)
+    torch.cuda.set_stream(stream)
     bits, M = cfg.bits, cfg.M
 
     # Offline weight quantization (timed once, reported separately).
@@ -447,6 +545,9 @@ def main():
         "weight_quant_ms_offline": round(wq_ms, 3), "buffer_sets": R,
         "quant_error_rel_frobenius_vs_fp64": qerr,
     }
+    out["gpu_state_after_timing"] = gpu_state()
+    log("library int8 GEMM on the %s shape (context)" % dom.name)
+    out["context_library_int8_gemm"] = library_int8_gemm(torch, M, dom.N, dom.K)
     log("offline weight quantizer rules on %s" % dom.name)
     out["weight_quantizer"] = offline_weight_quant(rq, torch, g["W"][dom.name], bits, dev)
     if not args.no_cpu_baseline:
