@@ -151,6 +151,45 @@ def test_gemm_dequant_parity(M, N, K, bits, io, with_bias):
     assert np.array_equal(got, ref)
 
 
+# Around the launcher's choice between four waves per tile and eight waves per tile (two
+# groups splitting the k steps; taken when there are no more tiles than CUs and at least 16
+# k steps of 64 bytes): both sides of the tile-count and step-count limits, ragged M and N.
+SPLIT_CASES = [(1000, 1040, 1024, 8),    # 36 tiles, 16 steps: split
+               (1000, 1040, 896, 8),     # 14 steps: not split
+               (770, 2064, 2048, 4),     # 68 tiles, 16 steps of int4: split
+               (4096, 2048, 1024, 8),    # exactly 256 tiles: split
+               (4096, 2064, 1024, 8)]    # 272 tiles: not split
+
+
+@pytest.mark.parametrize("M,N,K,bits", SPLIT_CASES)
+@pytest.mark.parametrize("layout", ["rows", "tiled"])
+def test_gemm_split_choice_parity(M, N, K, bits, layout):
+    need_gpu()
+    print("split-choice case M=%d N=%d K=%d bits=%d %s" % (M, N, K, bits, layout), flush=True)
+    rng = np.random.default_rng(M + 3 * N + K + bits)
+    A = _random_codes(rng, M, K, bits)
+    B = _random_codes(rng, N, K, bits)
+    packed = oracle.pack_codes(A, bits)
+    if layout == "tiled":
+        Ad = torch.from_numpy(tile_codes(packed, M, K, bits, pad_fill=0x77)).cuda()
+        xl = rq.RQ_X_TILED
+    else:
+        Ad = torch.from_numpy(packed).cuda()
+        xl = rq.RQ_X_ROWS
+    Bd = torch.from_numpy(oracle.pack_codes(B, bits)).cuda()
+    sx = (rng.random(M) * 0.05).astype(np.float32)
+    sw = (rng.random(N) * 2e-4).astype(np.float32)
+    b = rng.normal(0, 0.01, N).astype(np.float32)
+    dev = lambda a: torch.from_numpy(a).cuda()
+    acc = rq.gemm_s32(Ad, Bd, bits=bits, K=K, x_layout=xl, M=M)
+    Y = rq.gemm_dequant(Ad, dev(sx), Bd, dev(sw), dev(b), bits=bits, K=K, x_layout=xl)
+    torch.cuda.synchronize()
+    rows = _sample_rows(M, M + N) if M * N * K > 2e9 else np.arange(M)
+    ref_acc = oracle.gemm_s32(np.ascontiguousarray(A[rows]), B)
+    assert np.array_equal(acc.cpu().numpy()[rows], ref_acc)
+    assert np.array_equal(bits_from_dev(Y)[rows], oracle.epilogue(ref_acc, sx[rows], sw, b, oracle.F16))
+
+
 # Shapes the launcher sends to its 256 x 256-tile kernel (K of at least 1536 bytes of codes and
 # at least 192 such tiles), ragged in M and N; compared on sampled rows (all N columns).
 WIDE_CASES = [(2048, 6144, 1536, 8), (1900, 6160, 1536, 8), (2000, 6144, 3072, 4)]

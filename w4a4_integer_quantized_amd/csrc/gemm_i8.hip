@@ -29,6 +29,10 @@
 //     (w << 4) & 0xF0F0F0F0 (even k) and w & 0xF0F0F0F0 (odd k): each byte is 16 * code,
 //     exact for codes in [-8, 7]. Both operands get the same k permutation, so the sum is
 //     unchanged; the accumulator is 256 * acc and an exact arithmetic shift by 8 recovers it.
+//   * Launches with no more tiles than CUs and at least 16 k steps put eight waves on each
+//     tile instead (one 512-thread workgroup per CU, 146 KB LDS): two groups of four take the
+//     even and the odd k steps in lockstep, each with its own half of a doubled ring, then swap
+//     halves of their accumulators through LDS so that each wave finishes one 32-row block.
 //   * Workgroup -> tile map is XCD-aware: workgroups are dispatched round-robin over the 8
 //     XCDs, so logical tile L runs on XCD L / ceil(tiles / 8); neighbouring tiles (same Xq
 //     row panel, all of Wq) then share one XCD's L2.
@@ -55,9 +59,8 @@ constexpr int kStages = 3;
 constexpr int kThreads = 256;
 constexpr int kTileX = kBM * kBKB;             // 16 KB
 constexpr int kStageBytes = (kBM + kBN) * kBKB;   // 24 KB
-constexpr int kScaleOff = kStages * kStageBytes;  // 72 KB
-constexpr int kLdsBytes = kScaleOff + (2 * kBN + kBM) * 4;
 constexpr int kLoadsPerStep = kStageBytes / 1024 / 4;   // wave-wide 1 KB copies per wave: 6
+constexpr int kNumCUs = 256;                   // MI355X
 
 enum OutKind { kOutS32 = 0, kOutF16 = 1, kOutBF16 = 2 };
 
@@ -98,12 +101,120 @@ __device__ __forceinline__ uint32_t pack2(float a, float b, int out) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-template <int BITS, int OUT, bool XT>
-__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
+// The tile's epilogue for NB consecutive 32-row blocks of this wave: acc[a][b] holds the
+// 32 x 32 accumulator block of W rows a*32.. and tile rows row0 + b*32... Lane l holds
+// D[n][m] for m = b*32 + l%32 and n = a*32 + 8*(r/4) + 4*(l/32) + r%4, r = 0..15. Either raw
+// int32 accumulators (OUT == kOutS32) or the dequantizing epilogue through `stage`, this wave's
+// LDS staging block of 32*NB rows x 256 B. `scales` holds the tile's w_scale [128], bias [128]
+// and x_scale [256], parked in LDS before the k loop.
+template <int BITS, int OUT, int NB>
+__device__ __forceinline__ void tile_epilogue(v16i (&acc)[4][NB], const float* scales, uint8_t* stage,
+                                              int row0, int lane, int m0, int n0, int M, int N,
+                                              void* __restrict__ Y) {
+  const int msub = lane & 31, half = lane >> 5;
+  if constexpr (OUT == kOutS32) {
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+      const int m = m0 + row0 + b * 32 + msub;
+      if (m >= M) continue;
+#pragma unroll
+      for (int a = 0; a < 4; a++)
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+          const int n = n0 + a * 32 + 8 * g + 4 * half;
+          if (n >= N) continue;
+          int v[4];
+#pragma unroll
+          for (int e = 0; e < 4; e++) v[e] = (BITS == 4) ? (acc[a][b][4 * g + e] >> 8) : acc[a][b][4 * g + e];
+          *reinterpret_cast<int4*>(static_cast<int32_t*>(Y) + (int64_t)m * N + n) = make_int4(v[0], v[1], v[2], v[3]);
+        }
+    }
+  } else {
+    const float* e_sw = scales;
+    const float* e_b = e_sw + kBN;
+    const float* e_sx = e_b + kBN;
+    float xs[NB];
+#pragma unroll
+    for (int b = 0; b < NB; b++) xs[b] = e_sx[row0 + b * 32 + msub];
+#pragma unroll
+    for (int a = 0; a < 4; a++) {
+      float4 s4[4], b4[4];
+#pragma unroll
+      for (int g = 0; g < 4; g++) {
+        const int col = a * 32 + 8 * g + 4 * half;
+        s4[g] = *reinterpret_cast<const float4*>(e_sw + col);
+        b4[g] = *reinterpret_cast<const float4*>(e_b + col);
+      }
+#pragma unroll
+      for (int g = 0; g < 4; g++) {
+        const int col = a * 32 + 8 * g + 4 * half;   // tile-local output column
+        const float ws[4] = {s4[g].x, s4[g].y, s4[g].z, s4[g].w};
+        const float bs[4] = {b4[g].x, b4[g].y, b4[g].z, b4[g].w};
+#pragma unroll
+        for (int b = 0; b < NB; b++) {
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            const int v = (BITS == 4) ? (acc[a][b][4 * g + e] >> 8) : acc[a][b][4 * g + e];
+            y[e] = __builtin_fmaf(static_cast<float>(v), __fmul_rn(ws[e], xs[b]), bs[e]);
+          }
+          uint2 o;
+          o.x = pack2(y[0], y[1], OUT);
+          o.y = pack2(y[2], y[3], OUT);
+          const int row = b * 32 + msub;
+          const int chunk = (col >> 3) ^ (row & 15);
+          // Rows r and r + 16 share a chunk position; their 8-byte halves are swapped so the
+          // 32 lanes of a write hit distinct banks (undone when the row is read back).
+          const int hpos = half ^ ((row >> 4) & 1);
+          *reinterpret_cast<uint2*>(stage + row * 256 + chunk * 16 + hpos * 8) = o;
+        }
+      }
+    }
+    // Read back whole rows (16 lanes x 16 B = one 256-byte row segment, 4 rows per read), all
+    // reads first, then the streaming stores. A wave's LDS operations complete in order, so the
+    // reads see its own writes above.
+    constexpr int kIt = 8 * NB;
+    uint4 v[kIt];
+#pragma unroll
+    for (int it = 0; it < kIt; it++) {
+      const int row = it * 4 + (lane >> 4);
+      v[it] = *reinterpret_cast<const uint4*>(stage + row * 256 + (lane & 15) * 16);
+      // Rows with bit 4 set hold their 8-byte halves swapped (see the writes); bit 4 of row is
+      // (it >> 2) & 1 for every lane, so this is a compile-time register swap.
+      if ((it >> 2) & 1) v[it] = make_uint4(v[it].z, v[it].w, v[it].x, v[it].y);
+    }
+#pragma unroll
+    for (int it = 0; it < kIt; it++) {
+      const int row = it * 4 + (lane >> 4);
+      const int m = m0 + row0 + row;
+      const int n = n0 + 8 * ((lane & 15) ^ (row & 15));
+      if (m < M && n < N) {
+        // Streaming store: Y is written once and not re-read here, so it should not evict
+        // the Wq / Xq panels that neighbouring tiles re-read from L2.
+        v4i* dst = reinterpret_cast<v4i*>(static_cast<uint16_t*>(Y) + (int64_t)m * N + n);
+        __builtin_nontemporal_store(__builtin_bit_cast(v4i, v[it]), dst);
+      }
+    }
+  }
+}
+
+// SPLIT = 1: four waves own the tile and walk all of K. SPLIT = 2: eight waves in two groups of
+// four; group g takes the k steps 2j + g (its own half of a doubled LDS ring, in lockstep with the
+// other group at every barrier), then the groups exchange halves of their accumulators through
+// LDS, each sums the 32-row block it finishes, and both run the epilogue on their half. It
+// puts a whole CU's two wave slots per SIMD on one tile, for launches with too few tiles to give
+// every CU two.
+template <int SPLIT>
+constexpr int lds_bytes() { return kStages * SPLIT * kStageBytes + (2 * kBN + kBM) * 4; }
+
+template <int BITS, int OUT, bool XT, int SPLIT>
+__global__ __launch_bounds__(kThreads * SPLIT, 2 / SPLIT) void gemm_kernel(
     const uint8_t* __restrict__ Xq, const float* __restrict__ sx, const uint8_t* __restrict__ Wq,
     const float* __restrict__ sw, const float* __restrict__ bias, void* __restrict__ Y, int M,
     int N, int Kb, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[lds_bytes<SPLIT>()];
+  constexpr int kRing = kStages * SPLIT * kStageBytes;   // also where the scales are parked
+  constexpr int kSlot = SPLIT * kStageBytes;              // one ring stage, all groups
 
   const int ntiles = tiles_m * tiles_n;
   const int per_xcd = (ntiles + 7) >> 3;
@@ -114,7 +225,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
   const int m0 = tm * kBM, n0 = tn * kBN;
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = wave_all & 3;          // wave within its group: tile rows wave*64 ..
+  const int grp = wave_all >> 2;          // k-step group (0 when SPLIT == 1)
 
   // Per-tile epilogue operands, fetched now so their latency hides behind the mainloop.
   float my_sw = 0.0f, my_b = 0.0f, my_sx = 0.0f;
@@ -124,7 +237,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
       my_sw = sw[n];
       my_b = bias ? bias[n] : 0.0f;
     }
-    if (m < M) my_sx = sx[m];
+    if (threadIdx.x < kBM && m < M) my_sx = sx[m];
   }
 
   v16i acc[4][2];
@@ -135,9 +248,12 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[a][b][r] = 0;
 
-  // Stage s holds the Xq tile (256 rows) then the Wq tile (128 rows), 64 B per row.
-  auto issue = [&](int stage, int k0) {
-    uint8_t* tX = lds + stage * kStageBytes;
+  // Stage s of this group holds the Xq tile (256 rows) then the Wq tile (128 rows), 64 B per
+  // row, for k step SPLIT*j + grp.
+  uint8_t* const ring = lds + grp * kStageBytes;
+  auto issue = [&](int stage, int j) {
+    const int k0 = (SPLIT * j + grp) * kBKB;
+    uint8_t* tX = ring + stage * kSlot;
     uint8_t* tW = tX + kTileX;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -160,7 +276,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
   // Fragments of one 32-byte k slice: 4 Wq row blocks and this wave's 2 Xq row blocks.
   const int rsub = lane & 31, fhalf = lane >> 5;
   auto read_frags = [&](int stage, int ks, v4i (&wf)[4], v4i (&xf)[2]) {
-    const uint8_t* tX = lds + stage * kStageBytes;
+    const uint8_t* tX = ring + stage * kSlot;
     const uint8_t* tW = tX + kTileX;
     const int chunk = 2 * ks + fhalf;
 #pragma unroll
@@ -201,16 +317,18 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
     }
   };
 
-  // Software-pipelined k loop over a ring of 3 LDS stages (step j lives in stage j % 3).
-  // Step kt: the slice-1 fragments of step kt are read and -- when LOAD -- the 6 direct-to-LDS
-  // loads of step kt+2 are issued under the 8 (int4: 16) MFMAs of slice 0; then -- when MID --
-  // the wave waits for its own loads of step kt+1 and for all its fragment reads, passes the
-  // workgroup barrier, and reads slice 0 of step kt+1 under the MFMAs of slice 1. LDS latency
+  // Software-pipelined k loop over a ring of 3 LDS stages (this group's step j lives in stage
+  // j % 3).
+  // Step j: the slice-1 fragments of step j are read and -- when LOAD -- the 6 direct-to-LDS
+  // loads of step j+2 are issued under the 8 (int4: 16) MFMAs of slice 0; then -- when MID --
+  // the wave waits for its own loads of step j+1 and for all its fragment reads, passes the
+  // workgroup barrier, and reads slice 0 of step j+1 under the MFMAs of slice 1. LDS latency
   // and the barrier therefore overlap matrix work instead of following it.
-  // Why the ring is race free: the loads issued in step kt fill stage (kt+2) % 3 = (kt-1) % 3,
-  // whose last reads (slice 1 of step kt-1) every wave completed before the barrier of step
-  // kt-1; the reads of stage (kt+1) % 3 follow the barrier of step kt, which every wave passes
-  // only after its loads of step kt+1 have landed.
+  // Why the ring is race free: the loads issued in step j fill stage (j+2) % 3 = (j-1) % 3,
+  // whose last reads (slice 1 of step j-1) every wave completed before the barrier of step
+  // j-1; the reads of stage (j+1) % 3 follow the barrier of step j, which every wave passes
+  // only after its loads of step j+1 have landed. With SPLIT = 2 both groups take the same
+  // number of steps, so every barrier is passed by all eight waves.
   constexpr int kMfmaPerSlice = BITS == 8 ? 8 : 16;
   auto body = [&](auto load_tag, auto mid_tag, int kt, v4i (&wf0)[4], v4i (&xf0)[2]) {
     constexpr bool LOAD = decltype(load_tag)::value;
@@ -218,7 +336,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
     const int cur = kt % kStages;
     v4i wf1[4], xf1[2];
     read_frags(cur, 1, wf1, xf1);
-    if constexpr (LOAD) issue((kt + 2) % kStages, (kt + 2) * kBKB);
+    if constexpr (LOAD) issue((kt + 2) % kStages, kt + 2);
     mfma_slice(wf0, xf0);
 #pragma unroll
     for (int i = 0; i < 6; i++) {
@@ -257,22 +375,22 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  const int nk = Kb / kBKB;
+  const int nk = Kb / kBKB / SPLIT;       // steps per group (the launcher checks divisibility)
   issue(0, 0);
   if (nk > 1) {
-    issue(1, kBKB);
+    issue(1, 1);
     asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
   } else {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   // The epilogue operands have landed too (they were requested first): park them in LDS.
   if constexpr (OUT != kOutS32) {
-    float* e_sw = reinterpret_cast<float*>(lds + kScaleOff);
+    float* e_sw = reinterpret_cast<float*>(lds + kRing);
     if (threadIdx.x < kBN) {
       e_sw[threadIdx.x] = my_sw;
       e_sw[kBN + threadIdx.x] = my_b;
     }
-    e_sw[2 * kBN + threadIdx.x] = my_sx;
+    if (threadIdx.x < kBM) e_sw[2 * kBN + threadIdx.x] = my_sx;
   }
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
@@ -284,93 +402,43 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
   body(std::false_type{}, std::false_type{}, kt, wf0, xf0);
   __syncthreads();
 
-  // Epilogue. Lane l of block (a, b) holds D[n][m] for m = b*32 + l%32 and
-  // n = a*32 + 8*(r/4) + 4*(l/32) + r%4, r = 0..15 (wave-local indices; the wave's tokens are
-  // rows wave*64 .. wave*64+63 of the tile).
-  const int msub = lane & 31, half = lane >> 5;
-  if constexpr (OUT == kOutS32) {
-#pragma unroll
-    for (int b = 0; b < 2; b++) {
-      const int m = m0 + wave * 64 + b * 32 + msub;
-      if (m >= M) continue;
+  const float* scales = reinterpret_cast<const float*>(lds + kRing);
+  if constexpr (SPLIT == 1) {
+    tile_epilogue<BITS, OUT, 2>(acc, scales, lds + wave * (64 * 256), wave * 64, lane, m0, n0, M, N, Y);
+  } else {
+    // Group g finishes row block b = g of its four waves' rows: it sends its partial sums of
+    // block 1 - g to the partner wave (wave_all ^ 4) and adds the partner's partials of block g.
+    // Exchange layout: [wave_all][a][r4][lane] of 16-byte int4 (conflict-free 16-byte accesses).
+    int4* xch = reinterpret_cast<int4*>(lds);
+    auto slot = [&](int w, int a, int r4) { return xch + ((w * 4 + a) * 4 + r4) * 64 + lane; };
+    auto finish = [&](auto keep_tag) {
+      constexpr int KB = decltype(keep_tag)::value;   // the block this group finishes
 #pragma unroll
       for (int a = 0; a < 4; a++)
 #pragma unroll
-        for (int g = 0; g < 4; g++) {
-          const int n = n0 + a * 32 + 8 * g + 4 * half;
-          if (n >= N) continue;
-          int v[4];
+        for (int r4 = 0; r4 < 4; r4++)
+          *slot(wave_all, a, r4) = make_int4(acc[a][1 - KB][4 * r4], acc[a][1 - KB][4 * r4 + 1],
+                                             acc[a][1 - KB][4 * r4 + 2], acc[a][1 - KB][4 * r4 + 3]);
+      __syncthreads();
+      v16i keep[4][1];
 #pragma unroll
-          for (int e = 0; e < 4; e++) v[e] = (BITS == 4) ? (acc[a][b][4 * g + e] >> 8) : acc[a][b][4 * g + e];
-          *reinterpret_cast<int4*>(static_cast<int32_t*>(Y) + (int64_t)m * N + n) = make_int4(v[0], v[1], v[2], v[3]);
+      for (int a = 0; a < 4; a++)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; r4++) {
+          const int4 o = *slot(wave_all ^ 4, a, r4);
+          keep[a][0][4 * r4] = acc[a][KB][4 * r4] + o.x;
+          keep[a][0][4 * r4 + 1] = acc[a][KB][4 * r4 + 1] + o.y;
+          keep[a][0][4 * r4 + 2] = acc[a][KB][4 * r4 + 2] + o.z;
+          keep[a][0][4 * r4 + 3] = acc[a][KB][4 * r4 + 3] + o.w;
         }
-    }
-  } else {
-    // The ring is free now; the scales were parked at kScaleOff before the k loop.
-    const float* e_sw = reinterpret_cast<const float*>(lds + kScaleOff);
-    const float* e_b = e_sw + kBN;
-    const float* e_sx = e_b + kBN;
-    uint8_t* stage = lds + wave * (64 * 256);     // this wave's 64 x 128 fp16 block
-    float xs[2];
-#pragma unroll
-    for (int b = 0; b < 2; b++) xs[b] = e_sx[wave * 64 + b * 32 + msub];
-#pragma unroll
-    for (int a = 0; a < 4; a++) {
-      float4 s4[4], b4[4];
-#pragma unroll
-      for (int g = 0; g < 4; g++) {
-        const int col = a * 32 + 8 * g + 4 * half;
-        s4[g] = *reinterpret_cast<const float4*>(e_sw + col);
-        b4[g] = *reinterpret_cast<const float4*>(e_b + col);
-      }
-#pragma unroll
-      for (int g = 0; g < 4; g++) {
-        const int col = a * 32 + 8 * g + 4 * half;   // tile-local output column
-        const float ws[4] = {s4[g].x, s4[g].y, s4[g].z, s4[g].w};
-        const float bs[4] = {b4[g].x, b4[g].y, b4[g].z, b4[g].w};
-#pragma unroll
-        for (int b = 0; b < 2; b++) {
-          float y[4];
-#pragma unroll
-          for (int e = 0; e < 4; e++) {
-            const int v = (BITS == 4) ? (acc[a][b][4 * g + e] >> 8) : acc[a][b][4 * g + e];
-            y[e] = __builtin_fmaf(static_cast<float>(v), __fmul_rn(ws[e], xs[b]), bs[e]);
-          }
-          uint2 o;
-          o.x = pack2(y[0], y[1], OUT);
-          o.y = pack2(y[2], y[3], OUT);
-          const int row = b * 32 + msub;
-          const int chunk = (col >> 3) ^ (row & 15);
-          // Rows r and r + 16 share a chunk position; their 8-byte halves are swapped so the
-          // 32 lanes of a write hit distinct banks (undone when the row is read back).
-          const int hpos = half ^ ((row >> 4) & 1);
-          *reinterpret_cast<uint2*>(stage + row * 256 + chunk * 16 + hpos * 8) = o;
-        }
-      }
-    }
-    // Read back whole rows (16 lanes x 16 B = one 256-byte row segment, 4 rows per read), all
-    // reads first, then the streaming stores. A wave's LDS operations complete in order, so the
-    // reads see its own writes above.
-    uint4 v[16];
-#pragma unroll
-    for (int it = 0; it < 16; it++) {
-      const int row = it * 4 + (lane >> 4);
-      v[it] = *reinterpret_cast<const uint4*>(stage + row * 256 + (lane & 15) * 16);
-      // Rows with bit 4 set hold their 8-byte halves swapped (see the writes); bit 4 of row is
-      // (it >> 2) & 1 for every lane, so this is a compile-time register swap.
-      if ((it >> 2) & 1) v[it] = make_uint4(v[it].z, v[it].w, v[it].x, v[it].y);
-    }
-#pragma unroll
-    for (int it = 0; it < 16; it++) {
-      const int row = it * 4 + (lane >> 4);
-      const int m = m0 + wave * 64 + row;
-      const int n = n0 + 8 * ((lane & 15) ^ (row & 15));
-      if (m < M && n < N) {
-        // Streaming store: Y is written once and not re-read here, so it should not evict
-        // the Wq / Xq panels that neighbouring tiles re-read from L2.
-        v4i* dst = reinterpret_cast<v4i*>(static_cast<uint16_t*>(Y) + (int64_t)m * N + n);
-        __builtin_nontemporal_store(__builtin_bit_cast(v4i, v[it]), dst);
-      }
+      __syncthreads();   // every exchange read is done before the staging below reuses LDS
+      tile_epilogue<BITS, OUT, 1>(keep, scales, lds + wave_all * (32 * 256), wave * 64 + KB * 32, lane,
+                                  m0, n0, M, N, Y);
+    };
+    if (grp == 0) {
+      finish(std::integral_constant<int, 0>{});
+    } else {
+      finish(std::integral_constant<int, 1>{});
     }
   }
 }
@@ -382,9 +450,19 @@ hipError_t launch(const void* Xq, const float* sx, const void* Wq, const float* 
   const int tiles_n = (int)((N + kBN - 1) / kBN);
   const int ntiles = tiles_m * tiles_n;
   const int grid = ((ntiles + 7) / 8) * 8;
-  hipLaunchKernelGGL((gemm_kernel<BITS, OUT, XT>), dim3(grid), dim3(kThreads), 0, st,
-                     static_cast<const uint8_t*>(Xq), sx, static_cast<const uint8_t*>(Wq), sw,
-                     bias, Y, (int)M, (int)N, (int)Kb, tiles_m, tiles_n);
+  // Too few tiles to give every CU two workgroups: put eight waves on each tile instead (the
+  // k steps split between two wave groups), when the steps divide evenly and are long enough
+  // (at least 8 per group) for the split to pay for the final exchange; measured 4-8% faster
+  // on 168-tile launches with 64 steps, and slower with 1 step per group.
+  if (ntiles <= kNumCUs && (Kb / kBKB) % 2 == 0 && Kb / kBKB >= 16) {
+    hipLaunchKernelGGL((gemm_kernel<BITS, OUT, XT, 2>), dim3(grid), dim3(2 * kThreads), 0, st,
+                       static_cast<const uint8_t*>(Xq), sx, static_cast<const uint8_t*>(Wq), sw,
+                       bias, Y, (int)M, (int)N, (int)Kb, tiles_m, tiles_n);
+  } else {
+    hipLaunchKernelGGL((gemm_kernel<BITS, OUT, XT, 1>), dim3(grid), dim3(kThreads), 0, st,
+                       static_cast<const uint8_t*>(Xq), sx, static_cast<const uint8_t*>(Wq), sw,
+                       bias, Y, (int)M, (int)N, (int)Kb, tiles_m, tiles_n);
+  }
   return hipGetLastError();
 }
 
