@@ -32,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, TOP/s
+PEAK_FP6_TOPS = 10100.0      # MI355X dense fp6 / fp4 MFMA, TFLOP/s (the W4A4 path's matrix cores)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
 MALL_BYTES = 256 << 20
 PEAK_F64_OPS = 39.3e12       # MI355X vector fp64, non-fused ops/s (78.6 TFLOP/s counts an FMA as 2)
@@ -46,7 +47,7 @@ def log(msg):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("gemm_i8.hip", "gemm_i8_wide.hip", "rotate_quant.hip"):
+    for f in ("gemm_common.h", "gemm_i8.hip", "gemm_i8_wide.hip", "gemm_fp6.hip", "rotate_quant.hip"):
         with open(os.path.join(ROOT, "w4a4_integer_quantized_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -345,6 +346,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--w4-fp6", action="store_true",
+                    help="run 4-bit codes on the FP6 matrix cores (FP6 code tiles) instead of the int8 ones")
     ap.add_argument("--mfma-summary", nargs=2, metavar=("COUNTER_CSV", "KERNEL_TRACE_CSV"),
                     help="reduce a rocprofv3 MFMA-utilization run of the GEMM and exit")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -381,6 +384,10 @@ def main():
     torch.cuda.set_stream(stream)
     bits, M = cfg.bits, cfg.M
 
+    # 4-bit codes run on the int8 matrix cores by default; --w4-fp6 runs them on the FP6 ones
+    # (weights and activations stored as FP6 tiles; identical results). On the W4A4 workload the
+    # FP6 GEMM is faster but its activation quantizer slower, and the step measured slower.
+    wl = rq.RQ_W_FP6 if bits == 4 and args.w4_fp6 else rq.RQ_W_ROWS
     # Offline weight quantization (timed once, reported separately).
     Wq, Ws, B = {}, {}, {}
     wq_ms = 0.0
@@ -388,7 +395,7 @@ def main():
         Wd = torch.from_numpy(g["W"][lin.name]).to(dev)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        Wq[lin.name], Ws[lin.name] = rq.quantize_weights(Wd, bits=bits)
+        Wq[lin.name], Ws[lin.name] = rq.quantize_weights(Wd, bits=bits, w_layout=wl)
         torch.cuda.synchronize()
         wq_ms += (time.perf_counter() - t0) * 1e3
         B[lin.name] = torch.from_numpy(g["bias"][lin.name]).to(dev)
@@ -398,18 +405,19 @@ def main():
     x_host = torch.from_numpy(g["x_bits"].view(np.int16)).view(tdt)
     set_bytes = x_host.numel() * 2
     for lin in cfg.linears:
-        set_bytes += M * lin.N * 2 + rq.workspace_size(M, lin.K, bits)
+        set_bytes += M * lin.N * 2 + rq.workspace_size(M, lin.K, bits, w_layout=wl)
     R = max(3, min(8, math.ceil(3 * MALL_BYTES / set_bytes)))
     sets = []
     for _ in range(R):
         s = {"X": x_host.to(dev), "Y": {}, "ws": {}}
         for lin in cfg.linears:
             s["Y"][lin.name] = torch.empty((M, lin.N), dtype=tdt, device=dev)
-            s["ws"][lin.name] = torch.empty((rq.workspace_size(M, lin.K, bits),), dtype=torch.uint8, device=dev)
+            s["ws"][lin.name] = torch.empty((rq.workspace_size(M, lin.K, bits, w_layout=wl),), dtype=torch.uint8, device=dev)
         sets.append(s)
     log("ring of %d buffer sets, %.0f MB each" % (R, set_bytes / 1e6))
-    cfgc = rq.make_cfg(bits)
-    cfg_tiled = rq.make_cfg(bits, x_layout=rq.RQ_X_TILED)
+    cfgc = rq.make_cfg(bits, w_layout=wl)
+    peak_gemm = PEAK_FP6_TOPS if wl == rq.RQ_W_FP6 else PEAK_INT8_TOPS
+    cfg_tiled = rq.make_cfg(bits, x_layout=rq.RQ_X_FP6 if wl == rq.RQ_W_FP6 else rq.RQ_X_TILED, w_layout=wl)
     xdt = rq.RQ_F16 if cfg.io == "f16" else rq.RQ_BF16
     sptr = stream.cuda_stream
 
@@ -424,8 +432,9 @@ def main():
         # The raw entry points take bare pointers: check every buffer's shape on the host first.
         assert X.shape == (M, lin.K) and X.dtype == tdt and X.is_contiguous(), (lin.name, X.shape)
         assert s["Y"][lin.name].shape == (M, lin.N), lin.name
-        assert s["ws"][lin.name].numel() >= rq.workspace_size(M, lin.K, bits), lin.name
-        assert Wq[lin.name].shape == rq.code_shape(lin.N, lin.K, bits), lin.name
+        assert s["ws"][lin.name].numel() >= rq.workspace_size(M, lin.K, bits, w_layout=wl), lin.name
+        assert Wq[lin.name].numel() * Wq[lin.name].element_size() == \
+            rq.rq_weight_bytes(lin.N, lin.K, cfgc), lin.name
         return X
 
     def step(i):
@@ -496,7 +505,7 @@ def main():
             "rotate_quant_hbm_frac": round(rq_bytes / (rq_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "gemm_us": round(gm_ms * 1e3, 2),
             "gemm_TOPS": round(ops / (gm_ms * 1e-3) / 1e12, 1),
-            "gemm_mfma_frac": round(ops / (gm_ms * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+            "gemm_mfma_frac": round(ops / (gm_ms * 1e-3) / 1e12 / peak_gemm, 4),
             "call_TOPS": round(ops / ((rq_ms + gm_ms) * 1e-3) / 1e12, 1),
             "call_int8_peak_frac": round(ops / ((rq_ms + gm_ms) * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
             "rotate_quant_alg_bytes": rq_bytes, "gemm_alg_bytes": gemm_bytes, "gemm_alg_ops": ops,
@@ -507,8 +516,9 @@ def main():
     dc = calls[dom.name]
     tr = traffic_from_counters(cfg.workload, "gemm")
     traffic = tr["bytes"] if tr else None
-    roofline = {"bound": "mfma", "kernel": "gemm_kernel (%s: %dx%dx%d, W%dA%d)" % (dom.name, M, dom.N, dom.K, bits, bits),
-                "achieved": dc["gemm_TOPS"], "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
+    kname = "gemm_fp6_kernel" if wl == rq.RQ_W_FP6 else "gemm_kernel"
+    roofline = {"bound": "mfma", "kernel": "%s (%s: %dx%dx%d, W%dA%d)" % (kname, dom.name, M, dom.N, dom.K, bits, bits),
+                "achieved": dc["gemm_TOPS"], "peak": peak_gemm, "unit": "TOP/s",
                 "frac": dc["gemm_mfma_frac"], "traffic": traffic,
                 "avg_launch_us": dc["gemm_us"], "alg_ops_per_launch": dc["gemm_alg_ops"],
                 "alg_bytes_per_launch": dc["gemm_alg_bytes"], "traffic_detail": tr}
@@ -537,7 +547,8 @@ def main():
         "metric": "rotq_linear TOPS (rotate+quant+GEMM) and % of MI355X INT8 MFMA peak",
         "value": round(tops, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": "int4 codes as fp6 e2m3" if wl == rq.RQ_W_FP6 else "int8",
+        "data": "synthetic",
         "config": {"workload": cfg.workload, "M": M, "K": cfg.K, "N": [l.N for l in cfg.linears],
                    "io": cfg.io, "bits": bits, "calls_per_step": nl},
         "int8_peak_frac": round(tops / PEAK_INT8_TOPS, 4),

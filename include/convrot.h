@@ -18,7 +18,7 @@
  *              code = round_half_even(fl(u * inv)); q_max = 127 (8-bit) or 7 (4-bit).
  *   storage    8-bit: int8 [rows, K]; 4-bit: uint8 [rows, K/2], two's-complement nibbles,
  *              low nibble = even k.
- *   activation code layouts (rq_qconfig.x_layout; weights are always row-major):
+ *   activation code layouts (rq_qconfig.x_layout):
  *              RQ_X_ROWS   row-major as above, rows * Kb bytes (Kb = K or K/2 bytes per row);
  *              RQ_X_TILED  the GEMM's tile order: 256-row panels, each split into 64-byte
  *                          k steps stored as [panel][step][256 rows][64 B]. Byte b of row m
@@ -26,6 +26,23 @@
  *                          Rows are padded to a multiple of 256 (pad rows hold no defined value
  *                          and are never used); rq_codes_bytes() gives the size. The GEMM's
  *                          operand loads are then whole contiguous 1 KB blocks.
+ *              RQ_X_FP6    4-bit codes as FP6 tiles (below), 256-row panels.
+ *   weight code layouts (rq_qconfig.w_layout):
+ *              RQ_W_ROWS   row-major int8 [N, K] / packed int4 [N, K/2];
+ *              RQ_W_FP6    4-bit codes as FP6 tiles, 128-row panels; rq_weight_bytes() gives
+ *                          the size. The GEMM then runs on the FP6 matrix cores (below).
+ *   FP6 tiles  Every 4-bit code q in [-7, 7] is exactly an FP6 E2M3 value (sign bit 5, exponent
+ *              bits 4..3 with bias 1, mantissa bits 2..0): 0 -> 0, 1 -> 8, 2 -> 16, 3 -> 20,
+ *              4 -> 24, 5 -> 26, 6 -> 28, 7 -> 30, plus 32 for negative codes. Products of two
+ *              codes and their sums stay exact integers in fp32 (|acc| <= 49 K < 2^24), so the
+ *              FP6 MFMA gives the int32 accumulator exactly, at twice the int8 rate. Layout, for
+ *              a panel height P: K is split into 64-code slices; slice s of rows
+ *              [pP, pP + P) is one block of P * 48 bytes at ((p * K/64) + s) * P * 48. Within a
+ *              row, the slice's codes 32h .. 32h + 31 (h = 0, 1) form a 24-byte string (code e
+ *              of the half at bits 6e .. 6e+5, little-endian). Bytes 0..15 of half h of tile row
+ *              r sit in plane 1 at r * 32 + 16 * (h ^ (r >> 3 & 1)); bytes 16..23 in plane 2,
+ *              which starts at P * 32, at r * 16 + 8 * (h ^ (r >> 4 & 1)). Pad rows hold no
+ *              defined value and are never used.
  *   epilogue   y = fma(f32(acc), fl(w_scale[n] * x_scale[m]), bias[n] or +0), rounded to
  *              nearest-even fp16 / bf16.
  *
@@ -68,7 +85,8 @@ typedef enum { RQ_F32 = 0, RQ_F16 = 1, RQ_BF16 = 2 } rq_dtype;
 
 enum { RQ_ROT_WHT = 1 };   /* normalized Walsh-Hadamard rotation, Sylvester order */
 
-enum { RQ_X_ROWS = 0, RQ_X_TILED = 1 };   /* activation code layouts (see above) */
+enum { RQ_X_ROWS = 0, RQ_X_TILED = 1, RQ_X_FP6 = 2 };   /* activation code layouts (see above) */
+enum { RQ_W_ROWS = 0, RQ_W_FP6 = 1 };                   /* weight code layouts (see above) */
 
 /* Weight-scale rules of rq_quantize_weights. Each picks a clipping threshold t per row and
  * then quantizes exactly as above with a replaced by t: inv = fl(q_max / t),
@@ -95,16 +113,25 @@ typedef struct {
                          rq_rotq_linear always uses RQ_X_TILED inside its workspace) */
   int32_t w_scale_mode; /* RQ_W_ABSMAX, RQ_W_MSE or RQ_W_TENSOR: the scale rule of
                            rq_quantize_weights (every other entry point ignores it) */
+  int32_t w_layout;     /* RQ_W_ROWS or RQ_W_FP6 (bits 4 only): layout of Wq for
+                           rq_quantize_weights, rq_rotq_linear and the GEMM entry points. The
+                           GEMM entry points need x_layout == RQ_X_FP6 exactly when w_layout is
+                           RQ_W_FP6; rq_rotq_linear picks its workspace layout to match. */
 } rq_qconfig;
 
 /* Bytes of activation codes for `rows` rows of length K in cfg's bits and x_layout
  * (0 if cfg is invalid or the sizes are out of range). */
 size_t rq_codes_bytes(int64_t rows, int64_t K, const rq_qconfig *cfg);
 
+/* Bytes of weight codes for N rows of length K in cfg's bits and w_layout (0 if cfg is invalid
+ * or the sizes are out of range). */
+size_t rq_weight_bytes(int64_t N, int64_t K, const rq_qconfig *cfg);
+
 /* Offline weight quantizer ("Quantization recipe": upcast to FP32, block-Hadamard transform,
  * per-row scales), with the scale rule cfg->w_scale_mode.
  *   W        [N, K] device, dtype w_dtype (RQ_F32, RQ_F16 or RQ_BF16)
- *   Wq       out: int8 [N, K] (bits 8) or uint8 [N, K/2] (bits 4)
+ *   Wq       out: rq_weight_bytes(N, K, cfg) bytes in cfg->w_layout: int8 [N, K] (bits 8) or
+ *            uint8 [N, K/2] (bits 4) row-major, or FP6 tiles
  *   w_scale  out: float [N] (RQ_W_TENSOR also uses it as scratch between its kernels)
  * Returns RQ_OK or a status; see the conventions above. */
 rq_status rq_quantize_weights(const void *W, int32_t w_dtype, int64_t N, int64_t K,
@@ -120,16 +147,16 @@ rq_status rq_quantize_weights(const void *W, int32_t w_dtype, int64_t N, int64_t
 rq_status rq_rotate_quantize(const void *X, int32_t x_dtype, int64_t M, int64_t K,
                              const rq_qconfig *cfg, void *Xq, float *x_scale, void *stream);
 
-/* Bytes of device workspace rq_rotq_linear needs: Xq in RQ_X_TILED layout
- * (rq_codes_bytes(M, K) with x_layout = RQ_X_TILED) followed by x_scale [M], each rounded up
- * to 256 bytes. Returns 0 if cfg is invalid. */
+/* Bytes of device workspace rq_rotq_linear needs: Xq in RQ_X_TILED layout (RQ_X_FP6 when
+ * cfg->w_layout is RQ_W_FP6; rq_codes_bytes(M, K) with that x_layout) followed by x_scale [M],
+ * each rounded up to 256 bytes. Returns 0 if cfg is invalid. */
 size_t rq_rotq_linear_workspace_size(int64_t M, int64_t K, const rq_qconfig *cfg);
 
 /* The quantized linear ("Quantization recipe": W8A8 / W4A4 operations with online activation
  * quantization; "What ConvRot changes"): rotate + quantize X, int8 MFMA GEMM against Wq,
  * fused dequantize + bias + fp16/bf16 store.
  *   X         [M, K] device, x_dtype RQ_F16 or RQ_BF16
- *   Wq        [N, K] int8 or [N, K/2] uint8 (from rq_quantize_weights with the same cfg)
+ *   Wq        codes in cfg->w_layout (from rq_quantize_weights with the same cfg)
  *   w_scale   [N] float
  *   bias      [N] float, or NULL (no bias)
  *   Y         out: [M, N], same dtype as X; must not overlap X, Wq or the workspace

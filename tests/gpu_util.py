@@ -88,3 +88,59 @@ def tile_codes(rowmajor: np.ndarray, M: int, K: int, bits: int, pad_fill: int = 
     out = np.full(Mp * Kb, pad_fill, dtype=np.uint8)
     out[_tiled_index(M, Kb)] = np.ascontiguousarray(rowmajor).view(np.uint8).reshape(M, Kb)
     return out
+
+
+# ---- FP6 tiles (4-bit codes stored as FP6 E2M3; layout documented in include/convrot.h) ----
+_FP6_MAG = np.array([0, 8, 16, 20, 24, 26, 28, 30], np.uint8)
+
+
+def _fp6_value_table() -> np.ndarray:
+    """Value of every 6-bit E2M3 pattern (sign bit 5, exponent bits 4..3 with bias 1, mantissa
+    bits 2..0; exponent 0 is subnormal: m / 8)."""
+    v = np.zeros(64, np.float64)
+    for p in range(64):
+        e, m = (p >> 3) & 3, p & 7
+        mag = m / 8.0 if e == 0 else 2.0 ** (e - 1) * (1 + m / 8.0)
+        v[p] = -mag if p & 32 else mag
+    return v
+
+
+_FP6_VALUE = _fp6_value_table()
+
+
+def _fp6_index(rows: int, K: int, P: int):
+    """Flat byte index of byte j (0..23) of the operand string of (row, slice, half), as arrays
+    [rows, K/64, 2, 24]."""
+    nsl = K // 64
+    r = np.arange(rows, dtype=np.int64)[:, None, None, None]
+    s = np.arange(nsl, dtype=np.int64)[None, :, None, None]
+    h = np.arange(2, dtype=np.int64)[None, None, :, None]
+    j = np.arange(24, dtype=np.int64)[None, None, None, :]
+    base = ((r // P) * nsl + s) * (P * 48)
+    rr = r % P
+    p1 = base + rr * 32 + 16 * (h ^ ((rr >> 3) & 1)) + j
+    p2 = base + P * 32 + rr * 16 + 8 * (h ^ ((rr >> 4) & 1)) + (j - 16)
+    return np.where(j < 16, p1, p2)
+
+
+def fp6_untile(flat: np.ndarray, rows: int, K: int, P: int) -> np.ndarray:
+    """FP6 tiles -> int8 codes [rows, K] (every value must be an integer in [-7, 7])."""
+    b = np.asarray(flat).view(np.uint8)[_fp6_index(rows, K, P)].astype(np.uint32)   # [rows, nsl, 2, 24]
+    g = b[..., 0::3] | (b[..., 1::3] << 8) | (b[..., 2::3] << 16)                      # 8 fields of 24 bits
+    pats = np.stack([(g >> (6 * i)) & 63 for i in range(4)], axis=-1)                 # [rows, nsl, 2, 8, 4]
+    vals = _FP6_VALUE[pats.reshape(rows, K)]
+    assert np.all(vals == np.rint(vals)) and np.all(np.abs(vals) <= 7)
+    return vals.astype(np.int8)
+
+
+def fp6_tile(codes: np.ndarray, P: int, pad_fill: int = 0x5A) -> np.ndarray:
+    """int8 codes [rows, K] in [-7, 7] -> flat FP6 tiles (pad rows filled with pad_fill)."""
+    rows, K = codes.shape
+    c = codes.astype(np.int64)
+    pats = (_FP6_MAG[np.abs(c)].astype(np.uint32) | np.where(c < 0, 32, 0).astype(np.uint32))
+    pats = pats.reshape(rows, K // 64, 2, 8, 4)
+    g = pats[..., 0] | (pats[..., 1] << 6) | (pats[..., 2] << 12) | (pats[..., 3] << 18)
+    b = np.stack([g & 255, (g >> 8) & 255, (g >> 16) & 255], axis=-1).reshape(rows, K // 64, 2, 24)
+    out = np.full((rows + P - 1) // P * P * (K // 64) * 48, pad_fill, np.uint8)
+    out[_fp6_index(rows, K, P)] = b.astype(np.uint8)
+    return out

@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import w4a4_integer_quantized_amd as rq
@@ -77,7 +78,8 @@ def test_valid_arguments_pass():
     (dict(N=0), rq.RQ_EUNSUPPORTED),
     (dict(bits=6), rq.RQ_EUNSUPPORTED),
     (dict(rot=64), rq.RQ_EUNSUPPORTED),
-    (dict(x_layout=2), rq.RQ_EINVAL),
+    (dict(x_layout=3), rq.RQ_EINVAL),
+    (dict(x_layout=rq.RQ_X_FP6), rq.RQ_EUNSUPPORTED),           # FP6 codes are 4-bit only
     (dict(kind=0), rq.RQ_EUNSUPPORTED),
     (dict(ws_bytes=100), rq.RQ_EWORKSPACE),
     (dict(Y=A + 100 * 2), rq.RQ_EINVAL),                      # Y overlaps X
@@ -112,7 +114,18 @@ def test_codes_bytes():
     assert rq.rq_codes_bytes(7, 4096, rq.make_cfg(4)) == 7 * 2048
     assert rq.rq_codes_bytes(0, 1024, tiled) == 0
     assert rq.rq_codes_bytes(5, 1000, rows) == 0                       # K % 128 != 0
-    assert rq.rq_codes_bytes(5, 1024, rq.make_cfg(8, x_layout=2)) == 0  # bad layout
+    assert rq.rq_codes_bytes(5, 1024, rq.make_cfg(8, x_layout=3)) == 0  # bad layout
+    # FP6 tiles: 48 bytes per 64 codes, rows padded to 256 (activations) or 128 (weights).
+    fp6x = rq.make_cfg(4, x_layout=rq.RQ_X_FP6)
+    assert rq.rq_codes_bytes(300, 1024, fp6x) == 512 * 16 * 48
+    assert rq.rq_codes_bytes(5, 1024, rq.make_cfg(8, x_layout=rq.RQ_X_FP6)) == 0   # 8-bit codes
+    fp6w = rq.make_cfg(4, w_layout=rq.RQ_W_FP6)
+    assert rq.rq_weight_bytes(100, 256, fp6w) == 128 * 4 * 48
+    assert rq.rq_weight_bytes(100, 256, rq.make_cfg(4)) == 100 * 128
+    assert rq.rq_weight_bytes(100, 256, rq.make_cfg(8)) == 100 * 256
+    assert rq.rq_weight_bytes(100, 256, rq.make_cfg(8, w_layout=rq.RQ_W_FP6)) == 0
+    # The fused call's workspace follows the weight layout.
+    assert rq.rq_rotq_linear_workspace_size(300, 1024, fp6w) == 512 * 16 * 48 + 1280
 
 
 def test_entry_points_reject_before_launch():
@@ -134,6 +147,15 @@ def test_entry_points_reject_before_launch():
     bad = rq.make_cfg(8, w_scale_mode=3)
     assert rq.rq_quantize_weights(A, rq.RQ_F32, 16, 128, bad, A + GB, A + 2 * GB, None) == rq.RQ_EINVAL
     assert rq.rq_gemm_s32(A, A + GB, 16, 32, 128, bad, A + 2 * GB, None) == rq.RQ_EINVAL
+    # FP6 activation codes need FP6 weight codes in the GEMM entry points, and vice versa.
+    fx = rq.make_cfg(4, x_layout=rq.RQ_X_FP6)
+    fw = rq.make_cfg(4, w_layout=rq.RQ_W_FP6)
+    assert rq.rq_gemm_s32(A, A + GB, 16, 32, 128, fx, A + 2 * GB, None) == rq.RQ_EINVAL
+    assert rq.rq_gemm_s32(A, A + GB, 16, 32, 128, fw, A + 2 * GB, None) == rq.RQ_EINVAL
+    assert rq.rq_quantize_weights(A, rq.RQ_F32, 16, 128, rq.make_cfg(8, w_layout=rq.RQ_W_FP6), A + GB,
+                                  A + 2 * GB, None) == rq.RQ_EUNSUPPORTED
+    assert rq.rq_quantize_weights(A, rq.RQ_F32, 16, 128, rq.make_cfg(4, w_layout=2), A + GB,
+                                  A + 2 * GB, None) == rq.RQ_EINVAL
     for mode in (rq.RQ_W_ABSMAX, rq.RQ_W_MSE, rq.RQ_W_TENSOR):
         c = rq.make_cfg(4, w_scale_mode=mode)
         assert rq.rq_quantize_weights(A, rq.RQ_F32, 0, 256, c, A + GB, A + 2 * GB, None) == rq.RQ_OK
@@ -152,3 +174,20 @@ def test_qconfig_struct_matches_header():
     fields = re.findall(r"int32_t\s+(\w+);", body)
     assert [f for f, _ in rq.rq_qconfig._fields_] == fields
     assert ctypes.sizeof(rq.rq_qconfig) == 4 * len(fields)
+
+
+def test_fp6_test_helpers_follow_e2m3():
+    """The tests' FP6 encoder/decoder against the E2M3 definition: every code in [-7, 7] maps to
+    the pattern whose value (sign, 2-bit exponent with bias 1, 3-bit mantissa) is the code."""
+    from tests.gpu_util import _FP6_MAG, _FP6_VALUE, fp6_tile, fp6_untile
+    for q in range(8):
+        p = int(_FP6_MAG[q])
+        e, m = (p >> 3) & 3, p & 7
+        assert (m / 8.0 if e == 0 else 2.0 ** (e - 1) * (1 + m / 8.0)) == q
+        assert _FP6_VALUE[p] == q and _FP6_VALUE[p | 32] == -q
+    rng = np.random.default_rng(0)
+    c = rng.integers(-7, 8, (300, 384)).astype(np.int8)
+    for P in (128, 256):
+        t = fp6_tile(c, P)
+        assert t.size == (300 + P - 1) // P * P * 6 * 48
+        assert np.array_equal(fp6_untile(t, 300, 384, P), c)

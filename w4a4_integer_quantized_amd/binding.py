@@ -22,7 +22,8 @@ _LIB_PATH = os.path.join(PKG, "libconvrot.so")
 RQ_OK, RQ_EINVAL, RQ_EUNSUPPORTED, RQ_EWORKSPACE, RQ_EHIP = range(5)
 RQ_F32, RQ_F16, RQ_BF16 = 0, 1, 2
 RQ_ROT_WHT = 1
-RQ_X_ROWS, RQ_X_TILED = 0, 1
+RQ_X_ROWS, RQ_X_TILED, RQ_X_FP6 = 0, 1, 2
+RQ_W_ROWS, RQ_W_FP6 = 0, 1
 RQ_W_ABSMAX, RQ_W_MSE, RQ_W_TENSOR = 0, 1, 2
 
 
@@ -34,7 +35,7 @@ class ConvRotError(RuntimeError):
 
 class rq_qconfig(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int32), ("rot_kind", ctypes.c_int32), ("rot_block", ctypes.c_int32),
-                ("x_layout", ctypes.c_int32), ("w_scale_mode", ctypes.c_int32)]
+                ("x_layout", ctypes.c_int32), ("w_scale_mode", ctypes.c_int32), ("w_layout", ctypes.c_int32)]
 
 
 _lib = None
@@ -72,6 +73,8 @@ def load():
     lib.rq_rotq_linear_workspace_size.restype = SZ
     lib.rq_codes_bytes.argtypes = [I64, I64, CFG]
     lib.rq_codes_bytes.restype = SZ
+    lib.rq_weight_bytes.argtypes = [I64, I64, CFG]
+    lib.rq_weight_bytes.restype = SZ
     lib.rq_status_string.argtypes = [ctypes.c_int]
     lib.rq_status_string.restype = ctypes.c_char_p
     lib.rq_last_error_detail.argtypes = []
@@ -95,8 +98,9 @@ def _check(status: int, where: str):
 
 
 def make_cfg(bits: int = 8, rot_block: int = 128, rot_kind: int = RQ_ROT_WHT,
-             x_layout: int = RQ_X_ROWS, w_scale_mode: int = RQ_W_ABSMAX) -> rq_qconfig:
-    return rq_qconfig(bits, rot_kind, rot_block, x_layout, w_scale_mode)
+             x_layout: int = RQ_X_ROWS, w_scale_mode: int = RQ_W_ABSMAX,
+             w_layout: int = RQ_W_ROWS) -> rq_qconfig:
+    return rq_qconfig(bits, rot_kind, rot_block, x_layout, w_scale_mode, w_layout)
 
 
 # ----------------------------------------------------------------------------- raw entry points
@@ -128,6 +132,10 @@ def rq_rotq_linear_workspace_size(M, K, cfg) -> int:
 
 def rq_codes_bytes(rows, K, cfg) -> int:
     return load().rq_codes_bytes(rows, K, ctypes.byref(cfg))
+
+
+def rq_weight_bytes(N, K, cfg) -> int:
+    return load().rq_weight_bytes(N, K, ctypes.byref(cfg))
 
 
 def rq_check_rotq_linear_args(X, x_dtype, M, K, Wq, w_scale, N, bias, cfg, Y, ws, ws_bytes) -> int:
@@ -174,27 +182,33 @@ def code_shape(rows: int, K: int, bits: int) -> Tuple[int, int]:
     return (rows, K if bits == 8 else K // 2)
 
 
-def workspace_size(M: int, K: int, bits: int = 8) -> int:
-    return rq_rotq_linear_workspace_size(M, K, make_cfg(bits))
+def workspace_size(M: int, K: int, bits: int = 8, w_layout: int = RQ_W_ROWS) -> int:
+    return rq_rotq_linear_workspace_size(M, K, make_cfg(bits, w_layout=w_layout))
 
 
-def quantize_weights(W, bits: int = 8, rot: int = 128, stream=None, w_scale_mode: int = RQ_W_ABSMAX):
-    """Offline: W [N, K] (f32/f16/bf16, device) -> (Wq int8 [N, K] | uint8 [N, K/2], w_scale f32 [N]).
-    w_scale_mode: RQ_W_ABSMAX (per-row absmax), RQ_W_MSE (per-row MSE-optimized clipping) or
-    RQ_W_TENSOR (one tensor-wise scale)."""
+def quantize_weights(W, bits: int = 8, rot: int = 128, stream=None, w_scale_mode: int = RQ_W_ABSMAX,
+                     w_layout: int = RQ_W_ROWS):
+    """Offline: W [N, K] (f32/f16/bf16, device) -> (Wq, w_scale f32 [N]). Wq is int8 [N, K] /
+    uint8 [N, K/2] (RQ_W_ROWS) or a flat uint8 buffer of rq_weight_bytes() holding FP6 tiles
+    (RQ_W_FP6, bits 4). w_scale_mode: RQ_W_ABSMAX (per-row absmax), RQ_W_MSE (per-row
+    MSE-optimized clipping) or RQ_W_TENSOR (one tensor-wise scale)."""
     torch = _torch()
     N, K = W.shape
-    Wq = torch.empty(code_shape(N, K, bits), dtype=torch.int8 if bits == 8 else torch.uint8, device=W.device)
+    cfg = make_cfg(bits, rot, w_scale_mode=w_scale_mode, w_layout=w_layout)
+    if w_layout == RQ_W_ROWS:
+        Wq = torch.empty(code_shape(N, K, bits), dtype=torch.int8 if bits == 8 else torch.uint8, device=W.device)
+    else:
+        Wq = torch.empty((max(rq_weight_bytes(N, K, cfg), 1),), dtype=torch.uint8, device=W.device)
     ws = torch.empty((N,), dtype=torch.float32, device=W.device)
-    _check(rq_quantize_weights(_dev(W, "W"), _dtype_code(W), N, K,
-                               make_cfg(bits, rot, w_scale_mode=w_scale_mode),
+    _check(rq_quantize_weights(_dev(W, "W"), _dtype_code(W), N, K, cfg,
                                Wq.data_ptr(), ws.data_ptr(), _stream(stream)), "rq_quantize_weights")
     return Wq, ws
 
 
 def rotate_quantize(X, bits: int = 8, rot: int = 128, stream=None, x_layout: int = RQ_X_ROWS):
     """Online step alone: X [M, K] -> (Xq, x_scale f32 [M]). Xq is [M, K] int8 / [M, K/2] uint8
-    (RQ_X_ROWS) or a flat uint8 buffer of rq_codes_bytes() in the tiled layout (RQ_X_TILED)."""
+    (RQ_X_ROWS) or a flat uint8 buffer of rq_codes_bytes() in the tiled layout (RQ_X_TILED) or
+    as FP6 tiles (RQ_X_FP6, bits 4)."""
     torch = _torch()
     M, K = X.shape
     cfg = make_cfg(bits, rot, x_layout=x_layout)
@@ -209,12 +223,13 @@ def rotate_quantize(X, bits: int = 8, rot: int = 128, stream=None, x_layout: int
 
 
 def rotq_linear(X, Wq, w_scale, bias=None, bits: int = 8, rot: int = 128, workspace=None,
-                out=None, stream=None):
-    """Y [M, N] = dequant(int GEMM(rotate+quantize(X), Wq)) + bias, in X's dtype."""
+                out=None, stream=None, w_layout: int = RQ_W_ROWS):
+    """Y [M, N] = dequant(int GEMM(rotate+quantize(X), Wq)) + bias, in X's dtype; N = len(w_scale).
+    w_layout must be the layout Wq was quantized in (RQ_W_FP6: the FP6 matrix-core path)."""
     torch = _torch()
     M, K = X.shape
-    N = Wq.shape[0]
-    cfg = make_cfg(bits, rot)
+    N = w_scale.shape[0]
+    cfg = make_cfg(bits, rot, w_layout=w_layout)
     need = rq_rotq_linear_workspace_size(M, K, cfg)
     if workspace is None:
         workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=X.device)
@@ -227,29 +242,32 @@ def rotq_linear(X, Wq, w_scale, bias=None, bits: int = 8, rot: int = 128, worksp
 
 
 def gemm_dequant(Xq, x_scale, Wq, w_scale, bias=None, bits: int = 8, K: Optional[int] = None,
-                 out_dtype=None, stream=None, x_layout: int = RQ_X_ROWS):
-    """Y [M, N] from codes; M = len(x_scale), K from Wq unless given."""
+                 out_dtype=None, stream=None, x_layout: int = RQ_X_ROWS, w_layout: int = RQ_W_ROWS):
+    """Y [M, N] from codes; M = len(x_scale), N = len(w_scale), K from Wq unless given (give K
+    for FP6 weight tiles)."""
     torch = _torch()
     M = x_scale.shape[0]
-    N = Wq.shape[0]
+    N = w_scale.shape[0]
     K = K if K is not None else (Wq.shape[1] if bits == 8 else 2 * Wq.shape[1])
     out_dtype = torch.float16 if out_dtype is None else out_dtype
     Y = torch.empty((M, N), dtype=out_dtype, device=Xq.device)
     _check(rq_gemm_dequant(_dev(Xq, "Xq"), _dev(x_scale, "x_scale"), _dev(Wq, "Wq"), _dev(w_scale, "w_scale"),
                            _dev(bias, "bias") if bias is not None else None, M, N, K,
-                           make_cfg(bits, x_layout=x_layout), Y.data_ptr(), _dtype_code(Y),
+                           make_cfg(bits, x_layout=x_layout, w_layout=w_layout), Y.data_ptr(), _dtype_code(Y),
                            _stream(stream)), "rq_gemm_dequant")
     return Y
 
 
 def gemm_s32(Xq, Wq, bits: int = 8, K: Optional[int] = None, stream=None,
-             x_layout: int = RQ_X_ROWS, M: Optional[int] = None):
-    """acc [M, N] int32; M = Xq.shape[0] for row-major codes (give M for the tiled layout)."""
+             x_layout: int = RQ_X_ROWS, M: Optional[int] = None, N: Optional[int] = None,
+             w_layout: int = RQ_W_ROWS):
+    """acc [M, N] int32; M = Xq.shape[0] and N = Wq.shape[0] for row-major codes (give M for the
+    tiled layouts, N and K for FP6 weight tiles)."""
     torch = _torch()
     M = Xq.shape[0] if M is None else M
-    N = Wq.shape[0]
+    N = Wq.shape[0] if N is None else N
     K = K if K is not None else (Wq.shape[1] if bits == 8 else 2 * Wq.shape[1])
     acc = torch.empty((M, N), dtype=torch.int32, device=Xq.device)
-    _check(rq_gemm_s32(_dev(Xq, "Xq"), _dev(Wq, "Wq"), M, N, K, make_cfg(bits, x_layout=x_layout),
+    _check(rq_gemm_s32(_dev(Xq, "Xq"), _dev(Wq, "Wq"), M, N, K, make_cfg(bits, x_layout=x_layout, w_layout=w_layout),
                        acc.data_ptr(), _stream(stream)), "rq_gemm_s32")
     return acc

@@ -39,10 +39,27 @@ int64_t elem_size(int32_t dt) { return dt == RQ_F32 ? 4 : 2; }
 
 int64_t code_bytes(int64_t rows, int64_t K, int bits) { return bits == 8 ? rows * K : rows * K / 2; }
 
-// Activation codes in a layout: the tiled layout pads the rows to whole 256-row panels.
+// FP6 tiles: 48 bytes per 64 codes, rows padded to whole panels.
+int64_t fp6_bytes(int64_t rows, int64_t K, int64_t panel) { return (rows + panel - 1) / panel * panel * (K / 64) * 48; }
+
+// Activation codes in a layout: the tiled layouts pad the rows to whole 256-row panels.
 int64_t x_code_bytes(int64_t rows, int64_t K, int bits, int32_t layout) {
+  if (layout == RQ_X_FP6) return fp6_bytes(rows, K, 256);
   const int64_t r = layout == RQ_X_TILED ? (rows + 255) / 256 * 256 : rows;
   return code_bytes(r, K, bits);
+}
+
+// Weight codes in a layout: FP6 tiles pad the rows to whole 128-row panels.
+int64_t w_code_bytes(int64_t rows, int64_t K, int bits, int32_t layout) {
+  return layout == RQ_W_FP6 ? fp6_bytes(rows, K, 128) : code_bytes(rows, K, bits);
+}
+
+// The activation layout the fused call uses inside its workspace: FP6 tiles to match FP6
+// weights, else the tiled int layout.
+int32_t fused_x_layout(const rq_qconfig* cfg) { return cfg->w_layout == RQ_W_FP6 ? RQ_X_FP6 : RQ_X_TILED; }
+
+int code_layout(int32_t x_layout) {
+  return x_layout == RQ_X_FP6 ? convrot::kCodeFp6X : x_layout == RQ_X_TILED ? convrot::kCodeTiled : convrot::kCodeRows;
 }
 
 int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
@@ -61,8 +78,12 @@ rq_status check_cfg(const rq_qconfig* cfg) {
     return fail(RQ_EUNSUPPORTED, "rot_kind = %d (supported: RQ_ROT_WHT)", cfg->rot_kind);
   if (cfg->rot_block != 128)
     return fail(RQ_EUNSUPPORTED, "rot_block = %d (supported: 128)", cfg->rot_block);
-  if (cfg->x_layout != RQ_X_ROWS && cfg->x_layout != RQ_X_TILED)
-    return fail(RQ_EINVAL, "x_layout = %d (RQ_X_ROWS or RQ_X_TILED)", cfg->x_layout);
+  if (cfg->x_layout != RQ_X_ROWS && cfg->x_layout != RQ_X_TILED && cfg->x_layout != RQ_X_FP6)
+    return fail(RQ_EINVAL, "x_layout = %d (RQ_X_ROWS, RQ_X_TILED or RQ_X_FP6)", cfg->x_layout);
+  if (cfg->w_layout != RQ_W_ROWS && cfg->w_layout != RQ_W_FP6)
+    return fail(RQ_EINVAL, "w_layout = %d (RQ_W_ROWS or RQ_W_FP6)", cfg->w_layout);
+  if ((cfg->x_layout == RQ_X_FP6 || cfg->w_layout == RQ_W_FP6) && cfg->bits != 4)
+    return fail(RQ_EUNSUPPORTED, "FP6 code layouts hold 4-bit codes only (bits = %d)", cfg->bits);
   if (cfg->w_scale_mode != RQ_W_ABSMAX && cfg->w_scale_mode != RQ_W_MSE &&
       cfg->w_scale_mode != RQ_W_TENSOR)
     return fail(RQ_EINVAL, "w_scale_mode = %d (RQ_W_ABSMAX, RQ_W_MSE or RQ_W_TENSOR)",
@@ -110,7 +131,8 @@ rq_status check_rotate_args(const void* X, int32_t dt, int64_t rows, int64_t K, 
   if (!S) return fail(RQ_EINVAL, "scale output is NULL");
   if ((reinterpret_cast<uintptr_t>(S) & 3u) != 0) return fail(RQ_EINVAL, "scale output is not 4-byte aligned");
   const int64_t xb = rows * K * elem_size(dt);
-  const int64_t qb = activations ? x_code_bytes(rows, K, cfg->bits, cfg->x_layout) : code_bytes(rows, K, cfg->bits);
+  const int64_t qb = activations ? x_code_bytes(rows, K, cfg->bits, cfg->x_layout)
+                                 : w_code_bytes(rows, K, cfg->bits, cfg->w_layout);
   if (overlap(X, xb, Q, qb) || overlap(X, xb, S, rows * 4) || overlap(Q, qb, S, rows * 4))
     return fail(RQ_EINVAL, "input, codes and scales must not overlap");
   return ok();
@@ -135,7 +157,7 @@ rq_status check_linear(const void* X, int32_t x_dtype, int64_t M, int64_t K, con
   const size_t need = rq_rotq_linear_workspace_size(M, K, cfg);
   if (ws_bytes < need)
     return fail(RQ_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
-  const int64_t xb = M * K * 2, wb = code_bytes(N, K, cfg->bits), yb = M * N * 2;
+  const int64_t xb = M * K * 2, wb = w_code_bytes(N, K, cfg->bits, cfg->w_layout), yb = M * N * 2;
   if (overlap(Y, yb, X, xb) || overlap(Y, yb, Wq, wb) || overlap(Y, yb, ws, (int64_t)need) ||
       overlap(Y, yb, w_scale, N * 4) || overlap(Y, yb, bias, N * 4))
     return fail(RQ_EINVAL, "Y overlaps an input or the workspace");
@@ -159,9 +181,12 @@ rq_status check_gemm(const void* Xq, const float* x_scale, const void* Wq, const
   if ((s = check_ptr(w_scale, "w_scale", out_elem != 4))) return s;
   if ((s = check_ptr(bias, "bias", false))) return s;
   if (out_elem != 4 && !x_scale) return fail(RQ_EINVAL, "x_scale is NULL");
+  if ((cfg->x_layout == RQ_X_FP6) != (cfg->w_layout == RQ_W_FP6))
+    return fail(RQ_EINVAL, "FP6 activation codes go with FP6 weight codes (x_layout %d, w_layout %d)",
+                cfg->x_layout, cfg->w_layout);
   const int64_t ob = M * N * out_elem;
   if (overlap(out, ob, Xq, x_code_bytes(M, K, cfg->bits, cfg->x_layout)) ||
-      overlap(out, ob, Wq, code_bytes(N, K, cfg->bits)) ||
+      overlap(out, ob, Wq, w_code_bytes(N, K, cfg->bits, cfg->w_layout)) ||
       overlap(out, ob, x_scale, M * 4) || overlap(out, ob, w_scale, N * 4) || overlap(out, ob, bias, N * 4))
     return fail(RQ_EINVAL, "output overlaps an input");
   return ok();
@@ -188,7 +213,13 @@ const char* rq_version(void) { return "0.1.0"; }
 
 size_t rq_rotq_linear_workspace_size(int64_t M, int64_t K, const rq_qconfig* cfg) {
   if (check_cfg(cfg) != RQ_OK || M < 0 || K <= 0) return 0;
-  return (size_t)(round256(x_code_bytes(M, K, cfg->bits, RQ_X_TILED)) + round256(M * 4));
+  return (size_t)(round256(x_code_bytes(M, K, cfg->bits, fused_x_layout(cfg))) + round256(M * 4));
+}
+
+size_t rq_weight_bytes(int64_t N, int64_t K, const rq_qconfig* cfg) {
+  if (check_cfg(cfg) != RQ_OK || N < 0 || N > kMaxRowsOrCols || K <= 0 || K > kMaxK || K % 128)
+    return 0;
+  return (size_t)w_code_bytes(N, K, cfg->bits, cfg->w_layout);
 }
 
 size_t rq_codes_bytes(int64_t rows, int64_t K, const rq_qconfig* cfg) {
@@ -201,13 +232,15 @@ rq_status rq_quantize_weights(const void* W, int32_t w_dtype, int64_t N, int64_t
                               const rq_qconfig* cfg, void* Wq, float* w_scale, void* stream) {
   rq_status s = check_rotate_args(W, w_dtype, N, K, cfg, Wq, w_scale, "W", false);
   if (s) return s;
+  const bool fp6 = cfg->w_layout == RQ_W_FP6;
   if (cfg->w_scale_mode != RQ_W_ABSMAX)
     return from_hip(convrot::launch_weight_quant(cfg->w_scale_mode == RQ_W_MSE ? convrot::kWScaleMse
                                                                                 : convrot::kWScaleTensor,
-                                                 W, w_dtype, N, K, cfg->bits, Wq, w_scale,
+                                                 W, w_dtype, N, K, cfg->bits, fp6, Wq, w_scale,
                                                  static_cast<hipStream_t>(stream)),
                     "weight_quant launch");
-  return from_hip(convrot::launch_rotate_quant(W, w_dtype, N, K, cfg->bits, false, Wq, w_scale,
+  return from_hip(convrot::launch_rotate_quant(W, w_dtype, N, K, cfg->bits,
+                                               fp6 ? convrot::kCodeFp6W : convrot::kCodeRows, Wq, w_scale,
                                                static_cast<hipStream_t>(stream)),
                   "rotate_quant launch");
 }
@@ -216,9 +249,8 @@ rq_status rq_rotate_quantize(const void* X, int32_t x_dtype, int64_t M, int64_t 
                              const rq_qconfig* cfg, void* Xq, float* x_scale, void* stream) {
   rq_status s = check_rotate_args(X, x_dtype, M, K, cfg, Xq, x_scale, "X", true);
   if (s) return s;
-  return from_hip(convrot::launch_rotate_quant(X, x_dtype, M, K, cfg->bits,
-                                               cfg->x_layout == RQ_X_TILED, Xq, x_scale,
-                                               static_cast<hipStream_t>(stream)),
+  return from_hip(convrot::launch_rotate_quant(X, x_dtype, M, K, cfg->bits, code_layout(cfg->x_layout),
+                                               Xq, x_scale, static_cast<hipStream_t>(stream)),
                   "rotate_quant launch");
 }
 
@@ -236,12 +268,16 @@ rq_status rq_rotq_linear(const void* X, int32_t x_dtype, int64_t M, int64_t K, c
   rq_status s = check_linear(X, x_dtype, M, K, Wq, w_scale, N, bias, cfg, Y, workspace, ws_bytes);
   if (s || M == 0) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // The workspace holds the codes in the tiled layout, then x_scale.
+  // The workspace holds the codes in the tiled layout (FP6 tiles with FP6 weights), then x_scale.
+  const int32_t xl = fused_x_layout(cfg);
   uint8_t* Xq = static_cast<uint8_t*>(workspace);
-  float* sx = reinterpret_cast<float*>(Xq + round256(x_code_bytes(M, K, cfg->bits, RQ_X_TILED)));
-  if ((s = from_hip(convrot::launch_rotate_quant(X, x_dtype, M, K, cfg->bits, true, Xq, sx, st),
+  float* sx = reinterpret_cast<float*>(Xq + round256(x_code_bytes(M, K, cfg->bits, xl)));
+  if ((s = from_hip(convrot::launch_rotate_quant(X, x_dtype, M, K, cfg->bits, code_layout(xl), Xq, sx, st),
                     "rotate_quant launch")))
     return s;
+  if (xl == RQ_X_FP6)
+    return from_hip(convrot::launch_gemm_fp6(Xq, sx, Wq, w_scale, bias, M, N, K, Y, x_dtype, nullptr, st),
+                    "gemm launch");
   return from_hip(convrot::launch_gemm(Xq, sx, Wq, w_scale, bias, M, N, K, cfg->bits, true, Y,
                                        x_dtype, nullptr, st),
                   "gemm launch");
@@ -255,6 +291,10 @@ rq_status rq_gemm_dequant(const void* Xq, const float* x_scale, const void* Wq,
     return fail(y_dtype == RQ_F32 ? RQ_EUNSUPPORTED : RQ_EINVAL, "Y dtype %d (supported: RQ_F16, RQ_BF16)", y_dtype);
   rq_status s = check_gemm(Xq, x_scale, Wq, w_scale, bias, M, N, K, cfg, Y, 2);
   if (s || M == 0) return s;
+  if (cfg->x_layout == RQ_X_FP6)
+    return from_hip(convrot::launch_gemm_fp6(Xq, x_scale, Wq, w_scale, bias, M, N, K, Y, y_dtype, nullptr,
+                                             static_cast<hipStream_t>(stream)),
+                    "gemm launch");
   return from_hip(convrot::launch_gemm(Xq, x_scale, Wq, w_scale, bias, M, N, K, cfg->bits,
                                        cfg->x_layout == RQ_X_TILED, Y, y_dtype, nullptr,
                                        static_cast<hipStream_t>(stream)),
@@ -265,6 +305,10 @@ rq_status rq_gemm_s32(const void* Xq, const void* Wq, int64_t M, int64_t N, int6
                       const rq_qconfig* cfg, int32_t* acc, void* stream) {
   rq_status s = check_gemm(Xq, nullptr, Wq, nullptr, nullptr, M, N, K, cfg, acc, 4);
   if (s || M == 0) return s;
+  if (cfg->x_layout == RQ_X_FP6)
+    return from_hip(convrot::launch_gemm_fp6(Xq, nullptr, Wq, nullptr, nullptr, M, N, K, acc, RQ_F16, acc,
+                                             static_cast<hipStream_t>(stream)),
+                    "gemm launch");
   return from_hip(convrot::launch_gemm(Xq, nullptr, Wq, nullptr, nullptr, M, N, K, cfg->bits,
                                        cfg->x_layout == RQ_X_TILED, acc, RQ_F16, acc,
                                        static_cast<hipStream_t>(stream)),

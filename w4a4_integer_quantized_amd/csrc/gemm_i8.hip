@@ -41,35 +41,25 @@
 
 #include <type_traits>
 
+#include "gemm_common.h"
 #include "internal.h"
 
 namespace convrot {
 namespace {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+using namespace gemm;
 
-constexpr int kBM = 256;                       // tokens per tile
-constexpr int kBN = 128;                       // output features per tile
 constexpr int kBKB = 64;                       // K bytes per step
 constexpr int kStages = 3;
 constexpr int kThreads = 256;
 constexpr int kTileX = kBM * kBKB;             // 16 KB
 constexpr int kStageBytes = (kBM + kBN) * kBKB;   // 24 KB
 constexpr int kLoadsPerStep = kStageBytes / 1024 / 4;   // wave-wide 1 KB copies per wave: 6
-constexpr int kNumCUs = 256;                   // MI355X
-
-enum OutKind { kOutS32 = 0, kOutF16 = 1, kOutBF16 = 2 };
 
 // gfx950 LDS: 64 banks of 4 bytes, 16 lanes of a ds_read_b128 per cycle, and address bit 9
 // flips bank bit 5 (measured with the bank-conflict counter). With 64-byte rows that hardware
 // hash already separates rows r and r + 8, so the swizzle only spreads rows r..r+7 (bits 1-2).
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 3; }
-
-typedef __attribute__((address_space(3))) void lds_void;
 
 // One wave copies 16 rows x 64 B (1 KB) of a K-contiguous operand into LDS rows
 // [row0, row0 + 16) of a tile. Lane l fills LDS position (row0 + l/4, chunk l%4), which holds
@@ -88,114 +78,6 @@ __device__ __forceinline__ void copy_rows(const uint8_t* __restrict__ g, int64_t
 
 __device__ __forceinline__ v4i read_frag(const uint8_t* lds_tile, int row, int chunk) {
   return *reinterpret_cast<const v4i*>(lds_tile + row * kBKB + ((chunk ^ swz(row)) << 4));
-}
-
-// The epilogue rounds twice by definition: fma -> binary32, then binary32 -> fp16/bf16. The
-// empty asm pins each value as a binary32 register so the compiler cannot fuse the conversion
-// into the fma (v_fma_mix* rounds once, straight to fp16, which differs on rare ties).
-// gfx950 converts a pair with one v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32 (round to nearest even).
-__device__ __forceinline__ uint32_t pack2(float a, float b, int out) {
-  asm volatile("" : "+v"(a), "+v"(b));
-  const f32x2 v = {a, b};
-  if (out == kOutF16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
-
-// The tile's epilogue for NB consecutive 32-row blocks of this wave: acc[a][b] holds the
-// 32 x 32 accumulator block of W rows a*32.. and tile rows row0 + b*32... Lane l holds
-// D[n][m] for m = b*32 + l%32 and n = a*32 + 8*(r/4) + 4*(l/32) + r%4, r = 0..15. Either raw
-// int32 accumulators (OUT == kOutS32) or the dequantizing epilogue through `stage`, this wave's
-// LDS staging block of 32*NB rows x 256 B. `scales` holds the tile's w_scale [128], bias [128]
-// and x_scale [256], parked in LDS before the k loop.
-template <int BITS, int OUT, int NB>
-__device__ __forceinline__ void tile_epilogue(v16i (&acc)[4][NB], const float* scales, uint8_t* stage,
-                                              int row0, int lane, int m0, int n0, int M, int N,
-                                              void* __restrict__ Y) {
-  const int msub = lane & 31, half = lane >> 5;
-  if constexpr (OUT == kOutS32) {
-#pragma unroll
-    for (int b = 0; b < NB; b++) {
-      const int m = m0 + row0 + b * 32 + msub;
-      if (m >= M) continue;
-#pragma unroll
-      for (int a = 0; a < 4; a++)
-#pragma unroll
-        for (int g = 0; g < 4; g++) {
-          const int n = n0 + a * 32 + 8 * g + 4 * half;
-          if (n >= N) continue;
-          int v[4];
-#pragma unroll
-          for (int e = 0; e < 4; e++) v[e] = (BITS == 4) ? (acc[a][b][4 * g + e] >> 8) : acc[a][b][4 * g + e];
-          *reinterpret_cast<int4*>(static_cast<int32_t*>(Y) + (int64_t)m * N + n) = make_int4(v[0], v[1], v[2], v[3]);
-        }
-    }
-  } else {
-    const float* e_sw = scales;
-    const float* e_b = e_sw + kBN;
-    const float* e_sx = e_b + kBN;
-    float xs[NB];
-#pragma unroll
-    for (int b = 0; b < NB; b++) xs[b] = e_sx[row0 + b * 32 + msub];
-#pragma unroll
-    for (int a = 0; a < 4; a++) {
-      float4 s4[4], b4[4];
-#pragma unroll
-      for (int g = 0; g < 4; g++) {
-        const int col = a * 32 + 8 * g + 4 * half;
-        s4[g] = *reinterpret_cast<const float4*>(e_sw + col);
-        b4[g] = *reinterpret_cast<const float4*>(e_b + col);
-      }
-#pragma unroll
-      for (int g = 0; g < 4; g++) {
-        const int col = a * 32 + 8 * g + 4 * half;   // tile-local output column
-        const float ws[4] = {s4[g].x, s4[g].y, s4[g].z, s4[g].w};
-        const float bs[4] = {b4[g].x, b4[g].y, b4[g].z, b4[g].w};
-#pragma unroll
-        for (int b = 0; b < NB; b++) {
-          float y[4];
-#pragma unroll
-          for (int e = 0; e < 4; e++) {
-            const int v = (BITS == 4) ? (acc[a][b][4 * g + e] >> 8) : acc[a][b][4 * g + e];
-            y[e] = __builtin_fmaf(static_cast<float>(v), __fmul_rn(ws[e], xs[b]), bs[e]);
-          }
-          uint2 o;
-          o.x = pack2(y[0], y[1], OUT);
-          o.y = pack2(y[2], y[3], OUT);
-          const int row = b * 32 + msub;
-          const int chunk = (col >> 3) ^ (row & 15);
-          // Rows r and r + 16 share a chunk position; their 8-byte halves are swapped so the
-          // 32 lanes of a write hit distinct banks (undone when the row is read back).
-          const int hpos = half ^ ((row >> 4) & 1);
-          *reinterpret_cast<uint2*>(stage + row * 256 + chunk * 16 + hpos * 8) = o;
-        }
-      }
-    }
-    // Read back whole rows (16 lanes x 16 B = one 256-byte row segment, 4 rows per read), all
-    // reads first, then the streaming stores. A wave's LDS operations complete in order, so the
-    // reads see its own writes above.
-    constexpr int kIt = 8 * NB;
-    uint4 v[kIt];
-#pragma unroll
-    for (int it = 0; it < kIt; it++) {
-      const int row = it * 4 + (lane >> 4);
-      v[it] = *reinterpret_cast<const uint4*>(stage + row * 256 + (lane & 15) * 16);
-      // Rows with bit 4 set hold their 8-byte halves swapped (see the writes); bit 4 of row is
-      // (it >> 2) & 1 for every lane, so this is a compile-time register swap.
-      if ((it >> 2) & 1) v[it] = make_uint4(v[it].z, v[it].w, v[it].x, v[it].y);
-    }
-#pragma unroll
-    for (int it = 0; it < kIt; it++) {
-      const int row = it * 4 + (lane >> 4);
-      const int m = m0 + row0 + row;
-      const int n = n0 + 8 * ((lane & 15) ^ (row & 15));
-      if (m < M && n < N) {
-        // Streaming store: Y is written once and not re-read here, so it should not evict
-        // the Wq / Xq panels that neighbouring tiles re-read from L2.
-        v4i* dst = reinterpret_cast<v4i*>(static_cast<uint16_t*>(Y) + (int64_t)m * N + n);
-        __builtin_nontemporal_store(__builtin_bit_cast(v4i, v[it]), dst);
-      }
-    }
-  }
 }
 
 // SPLIT = 1: four waves own the tile and walk all of K. SPLIT = 2: eight waves in two groups of

@@ -11,17 +11,21 @@ enum InDtype { kF32 = 0, kF16 = 1, kBF16 = 2 };
 // Weight-scale rules (values of rq_qconfig.w_scale_mode).
 enum WScaleMode { kWScaleAbsmax = 0, kWScaleMse = 1, kWScaleTensor = 2 };
 
-// Rotate + quantize `rows` rows of length K (dtype `dt`) into codes Q (int8 or packed int4;
-// row-major, or the tiled layout of convrot.h when `tiled`) and one fp32 scale per row.
-// Arguments are pre-validated.
+// Code layouts written by the quantizers (convrot.h): row-major int8 / packed int4, the tiled
+// int layout (256-row panels), and FP6 tiles of 4-bit codes in 256-row (activation) or 128-row
+// (weight) panels.
+enum CodeLayout { kCodeRows = 0, kCodeTiled = 1, kCodeFp6X = 2, kCodeFp6W = 3 };
+
+// Rotate + quantize `rows` rows of length K (dtype `dt`) into codes Q in `layout` (a CodeLayout;
+// the FP6 layouts need bits == 4) and one fp32 scale per row. Arguments are pre-validated.
 hipError_t launch_rotate_quant(const void* X, int dt, int64_t rows, int64_t K, int bits,
-                               bool tiled, void* Q, float* S, hipStream_t stream);
+                               int layout, void* Q, float* S, hipStream_t stream);
 
 // The weight quantizer's MSE-clipped (kWScaleMse) or tensor-wise (kWScaleTensor) scale rule:
-// codes Wq (row-major int8 / packed int4) and one fp32 scale per row. Arguments are
-// pre-validated; N < 2^31.
+// codes Wq (row-major int8 / packed int4, or FP6 tiles of 128-row panels when fp6) and one fp32
+// scale per row. Arguments are pre-validated; N < 2^31.
 hipError_t launch_weight_quant(int mode, const void* W, int dt, int64_t N, int64_t K, int bits,
-                               void* Wq, float* S, hipStream_t stream);
+                               bool fp6, void* Wq, float* S, hipStream_t stream);
 
 // acc = Xq * Wq^T over K (codes of `bits` bits; Xq row-major or tiled when x_tiled, Wq
 // row-major), then either the dequantizing epilogue into Y (out_dt kF16 / kBF16) or, when
@@ -29,6 +33,12 @@ hipError_t launch_weight_quant(int mode, const void* W, int dt, int64_t N, int64
 hipError_t launch_gemm(const void* Xq, const float* sx, const void* Wq, const float* sw,
                        const float* bias, int64_t M, int64_t N, int64_t K, int bits,
                        bool x_tiled, void* Y, int out_dt, int32_t* acc32, hipStream_t stream);
+
+// 4-bit codes on the FP6 matrix cores: Xt and Wt in the FP6 tile layout of convrot.h (256-row
+// and 128-row panels). K % 128 == 0.
+hipError_t launch_gemm_fp6(const void* Xt, const float* sx, const void* Wt, const float* sw,
+                           const float* bias, int64_t M, int64_t N, int64_t K, void* Y,
+                           int out_dt, int32_t* acc32, hipStream_t stream);
 
 // The same GEMM on 256 x 256 tiles with 128-byte k steps (launch_gemm picks it for long K);
 // it needs Kb (K in bytes of codes) to be a multiple of 128 and at least 256.

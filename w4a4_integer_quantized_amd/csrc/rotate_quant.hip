@@ -233,13 +233,88 @@ __device__ __forceinline__ void quant_store32(uint8_t* dst, const float (&v)[4][
   }
 }
 
+// ---- FP6 tiles (4-bit codes stored as FP6 E2M3 for the FP6 matrix cores; see convrot.h) ----
+// Byte `b` (0..23) of the 24-byte operand string of row `row`, 64-element slice `s`, half `h`,
+// in panels of P rows: plane 1 (bytes 0..15, 32 B per row) then plane 2 (bytes 16..23, 16 B per
+// row), each with its two halves swapped on row bit 3 (plane 1) or bit 4 (plane 2).
+__device__ __forceinline__ int64_t fp6_offset(int64_t row, int s, int h, int b, int P, int nsl) {
+  const int64_t base = ((row / P) * nsl + s) * (int64_t)(P * 48);
+  const int rr = (int)(row % P);
+  if (b < 16) return base + rr * 32 + 16 * (h ^ ((rr >> 3) & 1)) + b;
+  return base + P * 32 + rr * 16 + 8 * (h ^ ((rr >> 4) & 1)) + (b - 16);
+}
+
+// FP6 E2M3 bytes of four codes: `sgn` holds the codes as two's-complement bytes (for the sign)
+// and `mag` their magnitudes 0..7; a byte permute looks the magnitudes up in
+// {0, 8, 16, 20, 24, 26, 28, 30} (1.0, 2.0, 1.5 * 2, 4.0, 1.25 * 4, 1.5 * 4, 1.75 * 4).
+__device__ __forceinline__ uint32_t fp6_bytes(uint32_t sgn, uint32_t mag) {
+  const uint32_t m = __builtin_amdgcn_perm(0x1E1C1A18u, 0x14100800u, mag);
+  return m | ((sgn >> 2) & 0x20202020u);
+}
+
+// Four 6-bit codes (the low six bits of each byte of c) -> one 24-bit field, code i at bit 6i.
+__device__ __forceinline__ uint32_t pack6x4(uint32_t c) {
+  uint32_t g = (c & 0x3Fu) | ((c >> 2) & 0xFC0u);
+  g |= (c >> 4) & 0x3F000u;
+  return g | ((c >> 6) & 0xFC0000u);
+}
+
+// Quantize the 32 consecutive values of v[0..3] (one lane's operand string: half h of slice s)
+// and store them as FP6 tiles.
+__device__ __forceinline__ void quant_store32_fp6(uint8_t* Q, int64_t row, int s, int h, int P, int nsl,
+                                                  const float (&v)[4][8], float tinv) {
+  uint32_t g[8];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+      uint32_t y[4], ya[4];
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const float pr = __fmul_rn(v[i][4 * q + r], tinv);
+        y[r] = __float_as_uint(__fadd_rn(pr, kRoundMagic));
+        ya[r] = __float_as_uint(__fadd_rn(fabsf(pr), kRoundMagic));
+      }
+      g[2 * i + q] = pack6x4(fp6_bytes(pack4_i8(y[0], y[1], y[2], y[3]), pack4_i8(ya[0], ya[1], ya[2], ya[3])));
+    }
+  }
+  const uint4 lo = make_uint4(g[0] | (g[1] << 24), (g[1] >> 8) | (g[2] << 16), (g[2] >> 16) | (g[3] << 8),
+                              g[4] | (g[5] << 24));
+  const uint2 hi = make_uint2((g[5] >> 8) | (g[6] << 16), (g[6] >> 16) | (g[7] << 8));
+  *reinterpret_cast<uint4*>(Q + fp6_offset(row, s, h, 0, P, nsl)) = lo;
+  *reinterpret_cast<uint2*>(Q + fp6_offset(row, s, h, 16, P, nsl)) = hi;
+}
+
+// The same for one piece of 8 consecutive values (elements 8q .. 8q+7 of the string, 6 bytes at
+// byte 6q), written as three 16-bit words (each lies within one plane).
+__device__ __forceinline__ void store_piece_fp6(uint8_t* Q, int64_t row, int s, int h, int q, int P, int nsl,
+                                                const float (&v)[8], float tinv) {
+  uint32_t g[2];
+#pragma unroll
+  for (int k = 0; k < 2; k++) {
+    uint32_t y[4], ya[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const float pr = __fmul_rn(v[4 * k + r], tinv);
+      y[r] = __float_as_uint(__fadd_rn(pr, kRoundMagic));
+      ya[r] = __float_as_uint(__fadd_rn(fabsf(pr), kRoundMagic));
+    }
+    g[k] = pack6x4(fp6_bytes(pack4_i8(y[0], y[1], y[2], y[3]), pack4_i8(ya[0], ya[1], ya[2], ya[3])));
+  }
+  const uint16_t w[3] = {static_cast<uint16_t>(g[0] & 0xFFFFu),
+                         static_cast<uint16_t>((g[0] >> 16) | ((g[1] & 0xFFu) << 8)),
+                         static_cast<uint16_t>(g[1] >> 8)};
+#pragma unroll
+  for (int k = 0; k < 3; k++) *reinterpret_cast<uint16_t*>(Q + fp6_offset(row, s, h, 6 * q + 2 * k, P, nsl)) = w[k];
+}
+
 // Register-resident kernel: BPQ blocks per quad, QPR quads per row, rows in slots of L lanes
 // (blockDim.x = 256 with 256 / L rows per workgroup, or blockDim.x = L > 64 with one row).
 template <int DT, int BITS, int BPQ>
 __global__ __launch_bounds__(256) void rotate_quant_kernel(const void* __restrict__ X, int64_t M,
                                                            int K, int L, int qpr,
                                                            uint8_t* __restrict__ Q,
-                                                           float* __restrict__ S, int tiled) {
+                                                           float* __restrict__ S, int layout) {
   __shared__ float red[4];
   const int tid = threadIdx.x;
   // L is a power of two <= 64 (256 / L rows per block) or the whole block (one row).
@@ -299,11 +374,16 @@ __global__ __launch_bounds__(256) void rotate_quant_kernel(const void* __restric
   float tinv, scale;
   row_scalars(a, qmax, tq, tinv, scale);
   if (active && qvalid) {
-    const int64_t Kb = (int64_t)K * BITS / 8;
 #pragma unroll
     for (int be = 0; be < BPQ; be++) {
-      const int64_t kb = ((int64_t)(be * qpr + q) * 128 + 32 * tq) * BITS / 8;
-      quant_store32<BITS>(Q + code_offset(row, kb, Kb, tiled), v[be], tinv);
+      if constexpr (BITS == 6) {
+        // Lane tq holds half tq & 1 of 64-element slice tq >> 1 of its block.
+        quant_store32_fp6(Q, row, 2 * (be * qpr + q) + (tq >> 1), tq & 1, layout, K >> 6, v[be], tinv);
+      } else {
+        const int64_t Kb = (int64_t)K * BITS / 8;
+        const int64_t kb = ((int64_t)(be * qpr + q) * 128 + 32 * tq) * BITS / 8;
+        quant_store32<BITS>(Q + code_offset(row, kb, Kb, layout != 0), v[be], tinv);
+      }
     }
   }
   if (active && t == 0) S[row] = scale;
@@ -317,7 +397,7 @@ __global__ __launch_bounds__(256) void rotate_quant_generic_kernel(const void* _
                                                                    int64_t M, int K,
                                                                    uint8_t* __restrict__ Q,
                                                                    float* __restrict__ S,
-                                                                   int tiled) {
+                                                                   int layout) {
   const int tid = threadIdx.x;
   const int t = tid & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (tid >> 6);
@@ -352,7 +432,12 @@ __global__ __launch_bounds__(256) void rotate_quant_generic_kernel(const void* _
       load8<DT>(X, row_elem0 + e, v);
       fwht8(v);
       cross_stages(v, m0, m1, m2, m3);
-      store_piece<BITS>(Q + code_offset(row, e * BITS / 8, (int64_t)K * BITS / 8, tiled), v, tinv);
+      if constexpr (BITS == 6) {
+        // Element e of the row: slice e / 64, half (e / 32) & 1, piece (e / 8) & 3 of the string.
+        store_piece_fp6(Q, row, (int)(e >> 6), (int)(e >> 5) & 1, (int)(e >> 3) & 3, layout, K >> 6, v, tinv);
+      } else {
+        store_piece<BITS>(Q + code_offset(row, e * BITS / 8, (int64_t)K * BITS / 8, layout != 0), v, tinv);
+      }
     }
   }
   if (t == 0) S[row] = scale;
@@ -365,38 +450,43 @@ struct RqShape {
 };
 
 template <int DT, int BITS, int BPQ>
-hipError_t launch_fast(const void* X, int64_t M, int K, RqShape sh, uint8_t* Q, float* S, int tiled,
+hipError_t launch_fast(const void* X, int64_t M, int K, RqShape sh, uint8_t* Q, float* S, int layout,
                        hipStream_t st) {
   const int threads = sh.L <= 64 ? 256 : sh.L;
   const int rows_per_block = threads / sh.L;
   const int64_t blocks = (M + rows_per_block - 1) / rows_per_block;
   hipLaunchKernelGGL((rotate_quant_kernel<DT, BITS, BPQ>), dim3((unsigned)blocks), dim3(threads), 0,
-                     st, X, M, K, sh.L, sh.qpr, Q, S, tiled);
+                     st, X, M, K, sh.L, sh.qpr, Q, S, layout);
   return hipGetLastError();
 }
 
 template <int DT, int BITS>
-hipError_t launch_bits(const void* X, int64_t M, int K, RqShape sh, uint8_t* Q, float* S, int tiled,
+hipError_t launch_bits(const void* X, int64_t M, int K, RqShape sh, uint8_t* Q, float* S, int layout,
                        hipStream_t st) {
   switch (sh.bpq) {
-    case 1: return launch_fast<DT, BITS, 1>(X, M, K, sh, Q, S, tiled, st);
-    case 2: return launch_fast<DT, BITS, 2>(X, M, K, sh, Q, S, tiled, st);
-    case 3: return launch_fast<DT, BITS, 3>(X, M, K, sh, Q, S, tiled, st);
-    case 4: return launch_fast<DT, BITS, 4>(X, M, K, sh, Q, S, tiled, st);
+    case 1: return launch_fast<DT, BITS, 1>(X, M, K, sh, Q, S, layout, st);
+    case 2: return launch_fast<DT, BITS, 2>(X, M, K, sh, Q, S, layout, st);
+    case 3: return launch_fast<DT, BITS, 3>(X, M, K, sh, Q, S, layout, st);
+    case 4: return launch_fast<DT, BITS, 4>(X, M, K, sh, Q, S, layout, st);
     default: {
       const int64_t blocks = (M + 3) / 4;
       hipLaunchKernelGGL((rotate_quant_generic_kernel<DT, BITS>), dim3((unsigned)blocks),
-                         dim3(256), 0, st, X, M, K, Q, S, tiled);
+                         dim3(256), 0, st, X, M, K, Q, S, layout);
       return hipGetLastError();
     }
   }
 }
 
+// `layout`: 0 row-major, 1 tiled int codes, or the panel height (256 or 128) of FP6 tiles when
+// FMT == 6 (4-bit codes stored as FP6).
 template <int DT>
-hipError_t launch_dt(const void* X, int64_t M, int K, int bits, RqShape sh, uint8_t* Q, float* S,
-                     int tiled, hipStream_t st) {
-  return bits == 8 ? launch_bits<DT, 8>(X, M, K, sh, Q, S, tiled, st)
-                   : launch_bits<DT, 4>(X, M, K, sh, Q, S, tiled, st);
+hipError_t launch_dt(const void* X, int64_t M, int K, int fmt, RqShape sh, uint8_t* Q, float* S,
+                     int layout, hipStream_t st) {
+  switch (fmt) {
+    case 8: return launch_bits<DT, 8>(X, M, K, sh, Q, S, layout, st);
+    case 4: return launch_bits<DT, 4>(X, M, K, sh, Q, S, layout, st);
+    default: return launch_bits<DT, 6>(X, M, K, sh, Q, S, layout, st);
+  }
 }
 
 }  // namespace
@@ -419,16 +509,20 @@ RqShape choose_rotate_quant_shape(int64_t K) {
   return {0, 0, 64};
 }
 
-hipError_t launch_rotate_quant(const void* X, int dt, int64_t rows, int64_t K, int bits, bool tiled,
+hipError_t launch_rotate_quant(const void* X, int dt, int64_t rows, int64_t K, int bits, int layout,
                                void* Q, float* S, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   const RqShape sh = choose_rotate_quant_shape(K);
   uint8_t* q = static_cast<uint8_t*>(Q);
-  const int t = tiled ? 1 : 0;
+  int fmt = bits, arg = layout == kCodeTiled ? 1 : 0;
+  if (layout == kCodeFp6X || layout == kCodeFp6W) {
+    fmt = 6;
+    arg = layout == kCodeFp6X ? 256 : 128;
+  }
   switch (dt) {
-    case kF32: return launch_dt<kF32>(X, rows, (int)K, bits, sh, q, S, t, stream);
-    case kF16: return launch_dt<kF16>(X, rows, (int)K, bits, sh, q, S, t, stream);
-    default: return launch_dt<kBF16>(X, rows, (int)K, bits, sh, q, S, t, stream);
+    case kF32: return launch_dt<kF32>(X, rows, (int)K, fmt, sh, q, S, arg, stream);
+    case kF16: return launch_dt<kF16>(X, rows, (int)K, fmt, sh, q, S, arg, stream);
+    default: return launch_dt<kBF16>(X, rows, (int)K, fmt, sh, q, S, arg, stream);
   }
 }
 

@@ -96,7 +96,24 @@ __device__ __forceinline__ float clamp_code(float p, float qmax) {
   return fminf(fmaxf(rintf(p), -qmax), qmax);
 }
 
-// Quantize one row against threshold t (t == 0: codes 0); returns the row's scale.
+// FP6 E2M3 pattern of a code in [-7, 7] (1.0, 2.0, 1.5 * 2, 4.0, 1.25 * 4, 1.5 * 4, 1.75 * 4).
+__device__ __forceinline__ uint32_t fp6_code(int q) {
+  const uint32_t mag = q < 0 ? (uint32_t)(-q) : (uint32_t)q;
+  const uint32_t m = (0x1E1C1A1814100800ull >> (8 * mag)) & 0xFFu;
+  return m | (q < 0 ? 0x20u : 0u);
+}
+
+// Byte `b` (0..23) of the FP6 operand string of row `row`, slice `s`, half `h` in 128-row weight
+// panels (the tile layout of convrot.h).
+__device__ __forceinline__ int64_t fp6w_offset(int64_t row, int s, int h, int b, int nsl) {
+  const int64_t base = ((row >> 7) * nsl + s) * (int64_t)(128 * 48);
+  const int rr = (int)(row & 127);
+  if (b < 16) return base + rr * 32 + 16 * (h ^ ((rr >> 3) & 1)) + b;
+  return base + 128 * 32 + rr * 16 + 8 * (h ^ ((rr >> 4) & 1)) + (b - 16);
+}
+
+// Quantize one row against threshold t (t == 0: codes 0); returns the row's scale. BITS = 6
+// stores 4-bit codes as FP6 weight tiles.
 template <int DT, int BITS>
 __device__ float quantize_row(const void* X, int64_t row, int64_t K, float t, uint8_t* Q, int lane) {
   const float qmax = BITS == 8 ? 127.0f : 7.0f;
@@ -110,6 +127,18 @@ __device__ float quantize_row(const void* X, int64_t row, int64_t K, float t, ui
     if constexpr (BITS == 8) {
       const uint16_t pair = static_cast<uint16_t>((q0 & 0xFF) | ((q1 & 0xFF) << 8));
       *reinterpret_cast<uint16_t*>(Q + row * K + 128 * (int64_t)b + 2 * lane) = pair;
+    } else if constexpr (BITS == 6) {
+      // Lanes 2m and 2m+1 hold elements 4m .. 4m+3 of the block: one 24-bit field (3 bytes)
+      // at byte 3 * (e % 32 / 4) of the string of slice 2b + e / 64, half (e / 32) & 1.
+      const uint32_t mine = fp6_code(q0) | (fp6_code(q1) << 6);
+      const uint32_t other = __shfl_xor(mine, 1);
+      if ((lane & 1) == 0) {
+        const uint32_t g = mine | (other << 12);
+        const int e = (4 * (lane >> 1)) & 63;
+        const int s = 2 * b + (lane >= 32 ? 1 : 0), h = (e >> 5) & 1, b0 = 3 * ((e & 31) >> 2);
+#pragma unroll
+        for (int k = 0; k < 3; k++) Q[fp6w_offset(row, s, h, b0 + k, (int)(K >> 6))] = static_cast<uint8_t>(g >> (8 * k));
+      }
     } else {
       Q[row * (K / 2) + 64 * (int64_t)b + lane] = static_cast<uint8_t>((q0 & 0xF) | ((q1 & 0xF) << 4));
     }
@@ -218,22 +247,26 @@ hipError_t launch_typed(int mode, const void* W, int64_t N, int64_t K, uint8_t* 
 }
 
 template <int DT>
-hipError_t launch_dt(int mode, const void* W, int64_t N, int64_t K, int bits, uint8_t* Q, float* S,
+hipError_t launch_dt(int mode, const void* W, int64_t N, int64_t K, int fmt, uint8_t* Q, float* S,
                      hipStream_t stream) {
-  return bits == 8 ? launch_typed<DT, 8>(mode, W, N, K, Q, S, stream)
-                   : launch_typed<DT, 4>(mode, W, N, K, Q, S, stream);
+  switch (fmt) {
+    case 8: return launch_typed<DT, 8>(mode, W, N, K, Q, S, stream);
+    case 4: return launch_typed<DT, 4>(mode, W, N, K, Q, S, stream);
+    default: return launch_typed<DT, 6>(mode, W, N, K, Q, S, stream);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_weight_quant(int mode, const void* W, int dt, int64_t N, int64_t K, int bits,
-                               void* Wq, float* S, hipStream_t stream) {
+                               bool fp6, void* Wq, float* S, hipStream_t stream) {
   if (N == 0) return hipSuccess;
   uint8_t* Q = static_cast<uint8_t*>(Wq);
+  const int fmt = fp6 ? 6 : bits;
   switch (dt) {
-    case kF32: return launch_dt<kF32>(mode, W, N, K, bits, Q, S, stream);
-    case kF16: return launch_dt<kF16>(mode, W, N, K, bits, Q, S, stream);
-    default: return launch_dt<kBF16>(mode, W, N, K, bits, Q, S, stream);
+    case kF32: return launch_dt<kF32>(mode, W, N, K, fmt, Q, S, stream);
+    case kF16: return launch_dt<kF16>(mode, W, N, K, fmt, Q, S, stream);
+    default: return launch_dt<kBF16>(mode, W, N, K, fmt, Q, S, stream);
   }
 }
 
