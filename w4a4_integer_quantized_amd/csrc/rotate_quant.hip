@@ -244,19 +244,23 @@ __device__ __forceinline__ int64_t fp6_offset(int64_t row, int s, int h, int b, 
   return base + P * 32 + rr * 16 + 8 * (h ^ ((rr >> 4) & 1)) + (b - 16);
 }
 
-// FP6 E2M3 bytes of four codes: `sgn` holds the codes as two's-complement bytes (for the sign)
-// and `mag` their magnitudes 0..7; a byte permute looks the magnitudes up in
-// {0, 8, 16, 20, 24, 26, 28, 30} (1.0, 2.0, 1.5 * 2, 4.0, 1.25 * 4, 1.5 * 4, 1.75 * 4).
-__device__ __forceinline__ uint32_t fp6_bytes(uint32_t sgn, uint32_t mag) {
-  const uint32_t m = __builtin_amdgcn_perm(0x1E1C1A18u, 0x14100800u, mag);
-  return m | ((sgn >> 2) & 0x20202020u);
+// FP6 E2M3 bytes of four codes given as two's-complement bytes in [-7, 7]: byte permutes look
+// the low three bits up in {0, 8, 16, 20, 24, 26, 28, 30} (0, 1.0, 2.0, 1.5 * 2, 4.0,
+// 1.25 * 4, 1.5 * 4, 1.75 * 4) for non-negative codes and in the patterns of -(8 - j) (sign bit
+// 32 set) for negative ones, and a bytewise select by the sign picks one.
+__device__ __forceinline__ uint32_t fp6_bytes(uint32_t d) {
+  const uint32_t j = d & 0x07070707u;
+  const uint32_t pos = __builtin_amdgcn_perm(0x1E1C1A18u, 0x14100800u, j);
+  const uint32_t neg = __builtin_amdgcn_perm(0x28303438u, 0x3A3C3E00u, j);
+  const uint32_t s = ((d >> 7) & 0x01010101u) * 0xFFu;   // 0xFF in the bytes of negative codes
+  return (neg & s) | (pos & ~s);
 }
 
 // Four 6-bit codes (the low six bits of each byte of c) -> one 24-bit field, code i at bit 6i.
 __device__ __forceinline__ uint32_t pack6x4(uint32_t c) {
-  uint32_t g = (c & 0x3Fu) | ((c >> 2) & 0xFC0u);
-  g |= (c >> 4) & 0x3F000u;
-  return g | ((c >> 6) & 0xFC0000u);
+  uint32_t g = (c & 0x3Fu) | ((c >> 2) & ~0x3Fu);
+  g = (g & 0xFFFu) | ((c >> 4) & ~0xFFFu);
+  return (g & 0x3FFFFu) | ((c >> 6) & ~0x3FFFFu);
 }
 
 // Quantize the 32 consecutive values of v[0..3] (one lane's operand string: half h of slice s)
@@ -268,14 +272,10 @@ __device__ __forceinline__ void quant_store32_fp6(uint8_t* Q, int64_t row, int s
   for (int i = 0; i < 4; i++) {
 #pragma unroll
     for (int q = 0; q < 2; q++) {
-      uint32_t y[4], ya[4];
+      uint32_t y[4];
 #pragma unroll
-      for (int r = 0; r < 4; r++) {
-        const float pr = __fmul_rn(v[i][4 * q + r], tinv);
-        y[r] = __float_as_uint(__fadd_rn(pr, kRoundMagic));
-        ya[r] = __float_as_uint(__fadd_rn(fabsf(pr), kRoundMagic));
-      }
-      g[2 * i + q] = pack6x4(fp6_bytes(pack4_i8(y[0], y[1], y[2], y[3]), pack4_i8(ya[0], ya[1], ya[2], ya[3])));
+      for (int r = 0; r < 4; r++) y[r] = code_bits(v[i][4 * q + r], tinv);
+      g[2 * i + q] = pack6x4(fp6_bytes(pack4_i8(y[0], y[1], y[2], y[3])));
     }
   }
   const uint4 lo = make_uint4(g[0] | (g[1] << 24), (g[1] >> 8) | (g[2] << 16), (g[2] >> 16) | (g[3] << 8),
@@ -292,14 +292,10 @@ __device__ __forceinline__ void store_piece_fp6(uint8_t* Q, int64_t row, int s, 
   uint32_t g[2];
 #pragma unroll
   for (int k = 0; k < 2; k++) {
-    uint32_t y[4], ya[4];
+    uint32_t y[4];
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-      const float pr = __fmul_rn(v[4 * k + r], tinv);
-      y[r] = __float_as_uint(__fadd_rn(pr, kRoundMagic));
-      ya[r] = __float_as_uint(__fadd_rn(fabsf(pr), kRoundMagic));
-    }
-    g[k] = pack6x4(fp6_bytes(pack4_i8(y[0], y[1], y[2], y[3]), pack4_i8(ya[0], ya[1], ya[2], ya[3])));
+    for (int r = 0; r < 4; r++) y[r] = code_bits(v[4 * k + r], tinv);
+    g[k] = pack6x4(fp6_bytes(pack4_i8(y[0], y[1], y[2], y[3])));
   }
   const uint16_t w[3] = {static_cast<uint16_t>(g[0] & 0xFFFFu),
                          static_cast<uint16_t>((g[0] >> 16) | ((g[1] & 0xFFu) << 8)),
