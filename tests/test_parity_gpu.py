@@ -190,8 +190,49 @@ def test_gemm_split_choice_parity(M, N, K, bits, layout):
     assert np.array_equal(bits_from_dev(Y)[rows], oracle.epilogue(ref_acc, sx[rows], sw, b, oracle.F16))
 
 
-# Shapes the launcher sends to its 256 x 256-tile kernel (K of at least 1536 bytes of codes and
-# at least 192 such tiles), ragged in M and N; compared on sampled rows (all N columns).
+# Around the launcher's choice of eight-wave 256 x 256 tiles (more 256 x 128 tiles than CUs and
+# at least 3072 bytes of K): ragged M; N ending on an idle (2176) or a partly filled (2192)
+# second half of the last 256-column tile; just below the K limit (2944 bytes: not taken).
+N2_CASES = [(4096, 2176, 3072, 8), (4100, 2080, 3072, 8), (4000, 2192, 6144, 4),
+            (4096, 2176, 2944, 8)]
+
+
+@pytest.mark.parametrize("M,N,K,bits", N2_CASES)
+@pytest.mark.parametrize("layout", ["rows", "tiled"])
+def test_gemm_n2_choice_parity(M, N, K, bits, layout):
+    need_gpu()
+    print("n2-choice case M=%d N=%d K=%d bits=%d %s" % (M, N, K, bits, layout), flush=True)
+    rng = np.random.default_rng(M + 5 * N + K + bits)
+    A = _random_codes(rng, M, K, bits)
+    B = _random_codes(rng, N, K, bits)
+    packed = oracle.pack_codes(A, bits)
+    if layout == "tiled":
+        Ad = torch.from_numpy(tile_codes(packed, M, K, bits, pad_fill=0x77)).cuda()
+        xl = rq.RQ_X_TILED
+    else:
+        Ad = torch.from_numpy(packed).cuda()
+        xl = rq.RQ_X_ROWS
+    Bd = torch.from_numpy(oracle.pack_codes(B, bits)).cuda()
+    sx = (rng.random(M) * 0.05).astype(np.float32)
+    sw = (rng.random(N) * 2e-4).astype(np.float32)
+    b = rng.normal(0, 0.01, N).astype(np.float32)
+    dev = lambda a: torch.from_numpy(a).cuda()
+    acc = rq.gemm_s32(Ad, Bd, bits=bits, K=K, x_layout=xl, M=M)
+    ys = {io: rq.gemm_dequant(Ad, dev(sx), Bd, dev(sw), dev(b), bits=bits, K=K, x_layout=xl,
+                              out_dtype=torch.float16 if io == "f16" else torch.bfloat16)
+          for io in ("f16", "bf16")}
+    torch.cuda.synchronize()
+    rows = _sample_rows(M, M + N)
+    ref_acc = oracle.gemm_s32(np.ascontiguousarray(A[rows]), B)
+    assert np.array_equal(acc.cpu().numpy()[rows], ref_acc)
+    for io, Y in ys.items():
+        ref = oracle.epilogue(ref_acc, sx[rows], sw, b, IO_CODE[io])
+        assert np.array_equal(bits_from_dev(Y)[rows], ref), io
+
+
+# Shapes the launcher sends to its 128-byte-row 256 x 256-tile kernel (row-major codes, K of
+# 1536-3071 bytes and at least 192 such tiles), ragged in M and N; compared on sampled rows
+# (all N columns).
 WIDE_CASES = [(2048, 6144, 1536, 8), (1900, 6160, 1536, 8), (2000, 6144, 3072, 4)]
 
 
@@ -204,7 +245,7 @@ def _sample_rows(M, seed):
 @pytest.mark.parametrize("M,N,K,bits", WIDE_CASES)
 def test_gemm_wide_tiles_parity(M, N, K, bits):
     need_gpu()
-    assert ((M + 255) // 256) * ((N + 255) // 256) >= 192 and K * bits // 8 >= 1536
+    assert ((M + 255) // 256) * ((N + 255) // 256) >= 192 and 1536 <= K * bits // 8 < 3072
     rng = np.random.default_rng(M + N + K + bits)
     A = _random_codes(rng, M, K, bits)
     B = _random_codes(rng, N, K, bits)

@@ -33,6 +33,10 @@
 //     tile instead (one 512-thread workgroup per CU, 146 KB LDS): two groups of four take the
 //     even and the odd k steps in lockstep, each with its own half of a doubled ring, then swap
 //     halves of their accumulators through LDS so that each wave finishes one 32-row block.
+//   * Launches with more tiles than CUs and at least 48 k steps use 256 x 256 tiles instead:
+//     eight waves in two groups of four share one 256-row Xq stage and each takes its own
+//     128-row half of a 256-row Wq stage (one 512-thread workgroup per CU, 132 KB LDS), which
+//     cuts the operand bytes the CU's load path moves per MFMA by a third.
 //   * Workgroup -> tile map is XCD-aware: workgroups are dispatched round-robin over the 8
 //     XCDs, so logical tile L runs on XCD L / ceil(tiles / 8); neighbouring tiles (same Xq
 //     row panel, all of Wq) then share one XCD's L2.
@@ -325,6 +329,194 @@ __global__ __launch_bounds__(kThreads * SPLIT, 2 / SPLIT) void gemm_kernel(
   }
 }
 
+// 256 x 256 tiles: eight waves in two groups of four; group g computes output columns
+// 128g .. 128g+127 of the tile (its half of a 256-row Wq stage) against the shared 256-row Xq
+// stage, so a CU moves two thirds of the operand bytes per MFMA of a 256 x 128 tile (32 KB
+// instead of 48 KB per 256 x 256 outputs and 64-byte k step).
+constexpr int kStageN2 = 2 * kBM * kBKB;              // 16 KB Xq + 16 KB Wq
+constexpr int kScaleBlk = (2 * kBN + kBM) * 4;        // one group's [w_scale | bias | x_scale]
+constexpr int kStageOut = 8 * 64 * 256;               // epilogue: 8 waves x 64 rows x 256 B
+constexpr int kLdsN2 = (kStageOut > kStages * kStageN2 ? kStageOut : kStages * kStageN2) + 2 * kScaleBlk;
+
+template <int BITS, int OUT, bool XT>
+__global__ __launch_bounds__(512, 1) void gemm_n2_kernel(
+    const uint8_t* __restrict__ Xq, const float* __restrict__ sx, const uint8_t* __restrict__ Wq,
+    const float* __restrict__ sw, const float* __restrict__ bias, void* __restrict__ Y, int M,
+    int N, int Kb, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsN2];
+  constexpr int kScales = kLdsN2 - 2 * kScaleBlk;
+
+  const int ntiles = tiles_m * tiles_n;
+  const int per_xcd = (ntiles + 7) >> 3;
+  const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (logical >= ntiles) return;
+  const int tm = logical / tiles_n;
+  const int tn = logical - tm * tiles_n;
+  const int m0 = tm * kBM, n0 = tn * 256;
+
+  const int lane = threadIdx.x & 63;
+  const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = wave_all & 3;
+  const int grp = wave_all >> 2;
+
+  float my_sw = 0.0f, my_b = 0.0f, my_sx = 0.0f;
+  if constexpr (OUT != kOutS32) {
+    const int n = n0 + (int)threadIdx.x, m = m0 + (int)(threadIdx.x & 255);
+    if (threadIdx.x < 256 && n < N) {
+      my_sw = sw[n];
+      my_b = bias ? bias[n] : 0.0f;
+    }
+    if (m < M) my_sx = sx[m];
+  }
+
+  v16i acc[4][2];
+#pragma unroll
+  for (int a = 0; a < 4; a++)
+#pragma unroll
+    for (int b = 0; b < 2; b++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[a][b][r] = 0;
+
+  auto issue = [&](int stage, int kt) {
+    const int k0 = kt * kBKB;
+    uint8_t* tX = lds + stage * kStageN2;
+    uint8_t* tW = tX + kTileX;
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+      const int row0 = (wave_all * 2 + i) * 16;
+      if constexpr (XT) {
+        const int r = row0 + (lane >> 2);
+        const int c = (lane & 3) ^ swz(r);
+        const uint8_t* src = Xq + (((int64_t)tm * (Kb >> 6) + (k0 >> 6)) << 14) + (r << 6) + 16 * c;
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(tX + row0 * kBKB), 16, 0, 0);
+      } else {
+        copy_rows(Xq, Kb, row0, m0, M, k0, tX, lane);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; i++) copy_rows(Wq, Kb, (wave_all * 2 + i) * 16, n0, N, k0, tW, lane);
+  };
+
+  const int rsub = lane & 31, fhalf = lane >> 5;
+  auto read_frags = [&](int stage, int ks, v4i (&wf)[4], v4i (&xf)[2]) {
+    const uint8_t* tX = lds + stage * kStageN2;
+    const uint8_t* tW = tX + kTileX;
+    const int chunk = 2 * ks + fhalf;
+#pragma unroll
+    for (int a = 0; a < 4; a++) wf[a] = read_frag(tW, grp * 128 + a * 32 + rsub, chunk);
+#pragma unroll
+    for (int b = 0; b < 2; b++) xf[b] = read_frag(tX, wave * 64 + b * 32 + rsub, chunk);
+  };
+  auto mfma_slice = [&](const v4i (&wf)[4], const v4i (&xf)[2]) {
+    if constexpr (BITS == 8) {
+#pragma unroll
+      for (int a = 0; a < 4; a++)
+#pragma unroll
+        for (int b = 0; b < 2; b++)
+          acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[a], xf[b], acc[a][b], 0, 0, 0);
+    } else {
+      v4i wlo[4], whi[4], xlo[2], xhi[2];
+#pragma unroll
+      for (int a = 0; a < 4; a++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          wlo[a][e] = (wf[a][e] << 4) & 0xF0F0F0F0;
+          whi[a][e] = wf[a][e] & 0xF0F0F0F0;
+        }
+#pragma unroll
+      for (int b = 0; b < 2; b++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          xlo[b][e] = (xf[b][e] << 4) & 0xF0F0F0F0;
+          xhi[b][e] = xf[b][e] & 0xF0F0F0F0;
+        }
+#pragma unroll
+      for (int a = 0; a < 4; a++)
+#pragma unroll
+        for (int b = 0; b < 2; b++) {
+          acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wlo[a], xlo[b], acc[a][b], 0, 0, 0);
+          acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(whi[a], xhi[b], acc[a][b], 0, 0, 0);
+        }
+    }
+  };
+
+  constexpr int kMfmaPerSlice = BITS == 8 ? 8 : 16;
+  auto body = [&](auto load_tag, auto mid_tag, int kt, v4i (&wf0)[4], v4i (&xf0)[2]) {
+    constexpr bool LOAD = decltype(load_tag)::value;
+    constexpr bool MID = decltype(mid_tag)::value;
+    const int cur = kt % kStages;
+    v4i wf1[4], xf1[2];
+    read_frags(cur, 1, wf1, xf1);
+    if constexpr (LOAD) issue((kt + 2) % kStages, kt + 2);
+    mfma_slice(wf0, xf0);
+#pragma unroll
+    for (int i = 0; i < 6; i++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    if constexpr (LOAD) {
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        if (i < kMfmaPerSlice - 6) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerSlice, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (MID) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if constexpr (LOAD) {
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags((kt + 1) % kStages, 0, wf0, xf0);
+    }
+    mfma_slice(wf1, xf1);
+    if constexpr (MID) {
+#pragma unroll
+      for (int i = 0; i < 6; i++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerSlice, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  const int nk = Kb / kBKB;
+  issue(0, 0);
+  if (nk > 1) {
+    issue(1, 1);
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  if constexpr (OUT != kOutS32) {
+    // Each group's scale block: [w_scale (its 128 columns) | bias | x_scale (all 256 rows)].
+    float* e0 = reinterpret_cast<float*>(lds + kScales);
+    if (threadIdx.x < 256) {
+      const int g = threadIdx.x >> 7, c = threadIdx.x & 127;
+      e0[g * (kScaleBlk / 4) + c] = my_sw;
+      e0[g * (kScaleBlk / 4) + kBN + c] = my_b;
+    }
+    e0[(threadIdx.x >> 8) * (kScaleBlk / 4) + 2 * kBN + (threadIdx.x & 255)] = my_sx;
+  }
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  v4i wf0[4], xf0[2];
+  read_frags(0, 0, wf0, xf0);
+  int kt = 0;
+  for (; kt + 2 < nk; kt++) body(std::true_type{}, std::true_type{}, kt, wf0, xf0);
+  if (kt + 1 < nk) body(std::false_type{}, std::true_type{}, kt++, wf0, xf0);
+  body(std::false_type{}, std::false_type{}, kt, wf0, xf0);
+  __syncthreads();
+  const float* scales = reinterpret_cast<const float*>(lds + kScales + grp * kScaleBlk);
+  tile_epilogue<BITS, OUT, 2>(acc, scales, lds + wave_all * (64 * 256), wave * 64, lane, m0, n0 + 128 * grp, M, N, Y);
+}
+
 template <int BITS, int OUT, bool XT>
 hipError_t launch(const void* Xq, const float* sx, const void* Wq, const float* sw,
                   const float* bias, int64_t M, int64_t N, int64_t Kb, void* Y, hipStream_t st) {
@@ -336,10 +528,19 @@ hipError_t launch(const void* Xq, const float* sx, const void* Wq, const float* 
   // k steps split between two wave groups), when the steps divide evenly and are long enough
   // (at least 8 per group) for the split to pay for the final exchange; measured 4-8% faster
   // on 168-tile launches with 64 steps, and slower with 1 step per group.
+  // Enough tiles to fill the machine and long K (at least 48 steps): 256 x 256 tiles halve the
+  // operand bytes each CU moves per MFMA; measured 6-12% faster at K = 3072-6144 bytes, and
+  // 5% slower at K = 1024 bytes, where the longer prologue and epilogue per tile dominate.
   if (ntiles <= kNumCUs && (Kb / kBKB) % 2 == 0 && Kb / kBKB >= 16) {
     hipLaunchKernelGGL((gemm_kernel<BITS, OUT, XT, 2>), dim3(grid), dim3(2 * kThreads), 0, st,
                        static_cast<const uint8_t*>(Xq), sx, static_cast<const uint8_t*>(Wq), sw,
                        bias, Y, (int)M, (int)N, (int)Kb, tiles_m, tiles_n);
+  } else if (ntiles > kNumCUs && Kb >= 3072) {
+    const int tiles_n2 = (int)((N + 255) / 256);
+    const int ntiles2 = tiles_m * tiles_n2;
+    hipLaunchKernelGGL((gemm_n2_kernel<BITS, OUT, XT>), dim3(((ntiles2 + 7) / 8) * 8), dim3(512), 0,
+                       st, static_cast<const uint8_t*>(Xq), sx, static_cast<const uint8_t*>(Wq), sw,
+                       bias, Y, (int)M, (int)N, (int)Kb, tiles_m, tiles_n2);
   } else {
     hipLaunchKernelGGL((gemm_kernel<BITS, OUT, XT, 1>), dim3(grid), dim3(kThreads), 0, st,
                        static_cast<const uint8_t*>(Xq), sx, static_cast<const uint8_t*>(Wq), sw,
@@ -370,14 +571,15 @@ hipError_t launch_gemm(const void* Xq, const float* sx, const void* Wq, const fl
                        bool x_tiled, void* Y, int out_dt, int32_t* acc32, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   const int64_t Kb = bits == 8 ? K : K / 2;
-  // Tiled activation codes (the fused path): this kernel measured fastest on every workload
-  // shape. Row-major codes: it is also the default, except for long K on enough tiles to fill
-  // the machine, where the 256 x 256 kernel's lower operand traffic per MFMA measured faster
-  // (by up to ~20%) than this kernel's 64-byte row segments.
+  // Tiled activation codes (the fused path): these kernels measured fastest on every workload
+  // shape. Row-major codes: they are also the default, except for K of 1536-3071 bytes on
+  // enough tiles to fill the machine, where the 128-byte-row 256 x 256 kernel's lower operand
+  // traffic per MFMA measured faster (by up to ~20%) than 64-byte row segments; from 3072 bytes
+  // on, the eight-wave 256 x 256 kernel here measured faster still (by ~15%).
   if (x_tiled)
     return launch_layout<true>(Xq, sx, Wq, sw, bias, M, N, Kb, bits, Y, out_dt, acc32, stream);
   const int64_t wide_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  if (wide_gemm_supported(Kb) && Kb >= 1536 && wide_tiles >= 192)
+  if (wide_gemm_supported(Kb) && Kb >= 1536 && Kb < 3072 && wide_tiles >= 192)
     return launch_gemm_wide(Xq, sx, Wq, sw, bias, M, N, K, bits, Y, out_dt, acc32, stream);
   return launch_layout<false>(Xq, sx, Wq, sw, bias, M, N, Kb, bits, Y, out_dt, acc32, stream);
 }
