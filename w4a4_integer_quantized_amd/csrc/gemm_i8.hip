@@ -449,16 +449,18 @@ __global__ __launch_bounds__(512, 1) void gemm_n2_kernel(
     read_frags(cur, 1, wf1, xf1);
     if constexpr (LOAD) issue((kt + 2) % kStages, kt + 2);
     mfma_slice(wf0, xf0);
+    // Two fragment reads after each of the first three MFMAs (measured 4-6% faster here than
+    // one read per MFMA: the last read has five MFMAs to land instead of two).
 #pragma unroll
-    for (int i = 0; i < 6; i++) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int i = 0; i < 3; i++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);        // DS read (slice 1)
     }
     if constexpr (LOAD) {
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        if (i < kMfmaPerSlice - 6) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // VMEM (global -> LDS)
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       }
     }
     __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerSlice, 0);
@@ -477,9 +479,9 @@ __global__ __launch_bounds__(512, 1) void gemm_n2_kernel(
     mfma_slice(wf1, xf1);
     if constexpr (MID) {
 #pragma unroll
-      for (int i = 0; i < 6; i++) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int i = 0; i < 3; i++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);      // DS read (next slice 0)
       }
     }
     __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerSlice, 0);
