@@ -46,6 +46,8 @@ def _load():
         lib.orc_gemm_s32.argtypes = [P, P, I64, I64, I64, P]
         lib.orc_gemm_s32.restype = I
         lib.orc_epilogue.argtypes = [P, P, P, P, I64, I64, I, P]
+        lib.orc_epilogue_act.argtypes = [P, P, P, P, I64, I64, I, I, P, P]
+        lib.orc_gelu_f64_array.argtypes = [P, I64, I, P]
         lib.orc_rotate_f64.argtypes = [P, I64, I64, P]
         for name in ("orc_f32_to_f16_array", "orc_f32_to_bf16_array",
                      "orc_f16_to_f32_array", "orc_bf16_to_f32_array"):
@@ -264,6 +266,37 @@ def epilogue(acc: np.ndarray, sx: np.ndarray, sw: np.ndarray, bias, out_dtype: i
     return Y
 
 
+ACT_NONE, ACT_GELU_ERF, ACT_GELU_TANH = 0, 1, 2
+
+
+def gelu_f64(v: np.ndarray, act: int) -> np.ndarray:
+    """GELU in binary64, element-wise (act 1: erf form, act 2: tanh form, 0: identity)."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    g = np.empty_like(v)
+    _load().orc_gelu_f64_array(_ptr(v), v.size, act, _ptr(g))
+    return g
+
+
+def epilogue_act(acc: np.ndarray, sx: np.ndarray, sw: np.ndarray, bias, out_dtype: int, act: int):
+    """The epilogue with the MLP activation fused: (Y bits, g64), where
+    Y = cast(f32(GELU64(fma(f32(acc), s_w[n]*s_x[m], bias[n])))) and g64 is GELU64 before the
+    two roundings (the value a one-ulp difference near a rounding midpoint is judged by)."""
+    acc = np.ascontiguousarray(acc, dtype=np.int32)
+    sx = np.ascontiguousarray(sx, dtype=np.float32)
+    sw = np.ascontiguousarray(sw, dtype=np.float32)
+    M, N = acc.shape
+    assert sx.shape == (M,) and sw.shape == (N,)
+    b = None
+    if bias is not None:
+        b = np.ascontiguousarray(bias, dtype=np.float32)
+        assert b.shape == (N,)
+    Y = np.empty((M, N), np.uint16)
+    g = np.empty((M, N), np.float64)
+    _load().orc_epilogue_act(_ptr(acc), _ptr(sx), _ptr(sw), _ptr(b) if b is not None else None,
+                             M, N, act, out_dtype, _ptr(Y), _ptr(g))
+    return Y, g
+
+
 # ---------------------------------------------------------------------------- whole path
 def quantize_weights(W: np.ndarray, bits: int = 8, rotate: bool = True, w_dtype: int = F32):
     """Offline step: (codes unpacked int8 [N, K], storage [N, K] or [N, K/2], w_scale [N])."""
@@ -272,15 +305,20 @@ def quantize_weights(W: np.ndarray, bits: int = 8, rotate: bool = True, w_dtype:
 
 
 def rotq_linear(X: np.ndarray, x_dtype: int, W_codes: np.ndarray, w_scale: np.ndarray, bias,
-                bits: int = 8, rotate: bool = True):
+                bits: int = 8, rotate: bool = True, act: int = ACT_NONE):
     """Online step on X bits [M, K] against already quantized weights.
 
-    Returns dict with x_codes, x_scale, acc, Y (uint16 bits in X's dtype).
+    Returns dict with x_codes, x_scale, acc, Y (uint16 bits in X's dtype) and, with an
+    activation, g64 (its binary64 value before rounding).
     """
     xc, xs, _ = quantize_rows(X, x_dtype, bits, rotate)
     acc = gemm_s32(xc, W_codes)
-    Y = epilogue(acc, xs, w_scale, bias, x_dtype)
-    return {"x_codes": xc, "x_scale": xs, "acc": acc, "Y": Y}
+    out = {"x_codes": xc, "x_scale": xs, "acc": acc}
+    if act == ACT_NONE:
+        out["Y"] = epilogue(acc, xs, w_scale, bias, x_dtype)
+    else:
+        out["Y"], out["g64"] = epilogue_act(acc, xs, w_scale, bias, x_dtype, act)
+    return out
 
 
 def linear_f64(X: np.ndarray, W: np.ndarray, bias) -> np.ndarray:

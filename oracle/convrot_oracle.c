@@ -21,7 +21,8 @@
  *   order h = 1, 2, 4, ..., 64; one absmax scale per row over all of K; q_max = 127 (int8)
  *   or 7 (int4), symmetric; round half to even; the normalization 1/sqrt(128) folded into
  *   the scale; zero rows get scale 0 and codes 0; int4 two per byte, low nibble = even k;
- *   int32 accumulation; epilogue y = fma(f32(acc), s_w*s_x, bias) rounded to fp16/bf16.
+ *   int32 accumulation; epilogue y = fma(f32(acc), s_w*s_x, bias) rounded to fp16/bf16;
+ *   the MLP activation (when fused into the epilogue) GELU in its erf or tanh form.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC (see build.py).
  * -ffp-contract=off matters: every fp32 operation below is one correctly rounded IEEE op.
@@ -360,6 +361,46 @@ void orc_epilogue(const int32_t *acc, const float *sx, const float *sw, const fl
       float sc = sw[n] * sx[m];
       float v = fmaf(af, sc, bias ? bias[n] : 0.0f);
       Y[m * N + n] = (out_dtype == ORC_F16) ? orc_f32_to_f16(v) : orc_f32_to_bf16(v);
+    }
+}
+
+/* GELU, the activation between the two linears of an MLP pair (the pages leave the MLP's
+ * activation unstated; the readings are the erf form for the ViT MLP and the tanh form for the
+ * DiT MLP). Evaluated in binary64 from the binary32 pre-activation v:
+ *   act 1, erf form:  0.5 v (1 + erf(v / sqrt 2)), written as 0.5 v erfc(-v / sqrt 2)
+ *   act 2, tanh form: 0.5 v (1 + tanh(u)) with u = sqrt(2 / pi) (v + 0.044715 v^3), written
+ *                     as v / (1 + exp(-2u))
+ * The erfc and logistic forms are the same functions without the cancellation of 1 + erf and
+ * 1 + tanh for negative v, so the result is accurate to a few binary64 ulps everywhere. */
+double orc_gelu_f64(double v, int act) {
+  if (act == 1) return 0.5 * v * erfc(-v / sqrt(2.0));
+  if (act == 2) {
+    const double u = sqrt(2.0 / acos(-1.0)) * (v + 0.044715 * v * v * v);
+    return v / (1.0 + exp(-2.0 * u));
+  }
+  return v;
+}
+
+void orc_gelu_f64_array(const double *v, int64_t n, int act, double *g) {
+  for (int64_t i = 0; i < n; i++) g[i] = orc_gelu_f64(v[i], act);
+}
+
+/* The epilogue with an activation: v = fma(f32(acc), fl(s_w * s_x), bias) as in orc_epilogue,
+ * then g = GELU(v) in binary64 (act 1 or 2; act 0: g = v), rounded to nearest even once to
+ * binary32 and then to binary16 / bfloat16. g64, when not NULL, receives the binary64 value
+ * before both roundings. */
+void orc_epilogue_act(const int32_t *acc, const float *sx, const float *sw, const float *bias,
+                      int64_t M, int64_t N, int act, int out_dtype, uint16_t *Y, double *g64) {
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < M; m++)
+    for (int64_t n = 0; n < N; n++) {
+      float af = (float)acc[m * N + n];
+      float sc = sw[n] * sx[m];
+      float v = fmaf(af, sc, bias ? bias[n] : 0.0f);
+      double g = orc_gelu_f64((double)v, act);
+      float gf = (float)g;
+      Y[m * N + n] = (out_dtype == ORC_F16) ? orc_f32_to_f16(gf) : orc_f32_to_bf16(gf);
+      if (g64) g64[m * N + n] = g;
     }
 }
 
