@@ -346,6 +346,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--unfused-gelu", action="store_true",
+                    help="MLP pairs: apply GELU as a separate torch op between the linears "
+                         "instead of in the first linear's epilogue (for comparison)")
     ap.add_argument("--w4-fp6", action="store_true",
                     help="run 4-bit codes on the FP6 matrix cores (FP6 code tiles) instead of the int8 ones")
     ap.add_argument("--mfma-summary", nargs=2, metavar=("COUNTER_CSV", "KERNEL_TRACE_CSV"),
@@ -415,18 +418,27 @@ def main():
             s["ws"][lin.name] = torch.empty((rq.workspace_size(M, lin.K, bits, w_layout=wl),), dtype=torch.uint8, device=dev)
         sets.append(s)
     log("ring of %d buffer sets, %.0f MB each" % (R, set_bytes / 1e6))
-    cfgc = rq.make_cfg(bits, w_layout=wl)
+    # MLP pairs: the GELU between the linears runs in the first linear's epilogue (or, with
+    # --unfused-gelu, as a torch op on the GPU between the two calls).
+    gelu_act = {"gelu_erf": rq.RQ_ACT_GELU_ERF, "gelu_tanh": rq.RQ_ACT_GELU_TANH}
+    act_of = {lin.name: rq.RQ_ACT_NONE for lin in cfg.linears}
+    if not args.unfused_gelu:
+        for lin in cfg.linears:
+            if lin.source in gelu_act:
+                act_of[lin.producer] = gelu_act[lin.source]
+    cfgc = {lin.name: rq.make_cfg(bits, w_layout=wl, act=act_of[lin.name]) for lin in cfg.linears}
     peak_gemm = PEAK_FP6_TOPS if wl == rq.RQ_W_FP6 else PEAK_INT8_TOPS
-    cfg_tiled = rq.make_cfg(bits, x_layout=rq.RQ_X_FP6 if wl == rq.RQ_W_FP6 else rq.RQ_X_TILED, w_layout=wl)
+    cfg_tiled = {lin.name: rq.make_cfg(bits, x_layout=rq.RQ_X_FP6 if wl == rq.RQ_W_FP6 else rq.RQ_X_TILED,
+                                       w_layout=wl, act=act_of[lin.name]) for lin in cfg.linears}
     xdt = rq.RQ_F16 if cfg.io == "f16" else rq.RQ_BF16
     sptr = stream.cuda_stream
 
     def lin_input(s, lin):
         if lin.source == "x":
             X = s["X"]
+        elif act_of[lin.producer] != rq.RQ_ACT_NONE:
+            X = s["Y"][lin.producer]          # the producer's epilogue applied the GELU
         else:
-            # MLP pair: the second layer's input is GELU of its producer's output (torch op on
-            # the GPU, outside the library)
             approx = "tanh" if lin.source == "gelu_tanh" else "none"
             X = torch.nn.functional.gelu(s["Y"][lin.producer], approximate=approx)
         # The raw entry points take bare pointers: check every buffer's shape on the host first.
@@ -434,7 +446,7 @@ def main():
         assert s["Y"][lin.name].shape == (M, lin.N), lin.name
         assert s["ws"][lin.name].numel() >= rq.workspace_size(M, lin.K, bits, w_layout=wl), lin.name
         assert Wq[lin.name].numel() * Wq[lin.name].element_size() == \
-            rq.rq_weight_bytes(lin.N, lin.K, cfgc), lin.name
+            rq.rq_weight_bytes(lin.N, lin.K, cfgc[lin.name]), lin.name
         return X
 
     def step(i):
@@ -443,7 +455,7 @@ def main():
             X = lin_input(s, lin)
             ws = s["ws"][lin.name]
             st = rq.rq_rotq_linear(X.data_ptr(), xdt, M, lin.K, Wq[lin.name].data_ptr(),
-                                   Ws[lin.name].data_ptr(), lin.N, B[lin.name].data_ptr(), cfgc,
+                                   Ws[lin.name].data_ptr(), lin.N, B[lin.name].data_ptr(), cfgc[lin.name],
                                    s["Y"][lin.name].data_ptr(), ws.data_ptr(), ws.numel(), sptr)
             if st != rq.RQ_OK:
                 raise rq.ConvRotError(st, "rq_rotq_linear", rq.load().rq_last_error_detail().decode())
@@ -474,12 +486,13 @@ def main():
             X = lin_input(s, lin)
             # The fused call's own layout: workspace = [tiled Xq | x_scale].
             xq = s["ws"][lin.name].data_ptr()
-            xs = xq + (rq.rq_codes_bytes(M, lin.K, cfg_tiled) + 255) // 256 * 256
+            ct = cfg_tiled[lin.name]
+            xs = xq + (rq.rq_codes_bytes(M, lin.K, ct) + 255) // 256 * 256
             evs[3 * c].record(stream)
-            st = rq.rq_rotate_quantize(X.data_ptr(), xdt, M, lin.K, cfg_tiled, xq, xs, sptr)
+            st = rq.rq_rotate_quantize(X.data_ptr(), xdt, M, lin.K, ct, xq, xs, sptr)
             evs[3 * c + 1].record(stream)
             st |= rq.rq_gemm_dequant(xq, xs, Wq[lin.name].data_ptr(), Ws[lin.name].data_ptr(),
-                                     B[lin.name].data_ptr(), M, lin.N, lin.K, cfg_tiled,
+                                     B[lin.name].data_ptr(), M, lin.N, lin.K, ct,
                                      s["Y"][lin.name].data_ptr(), xdt, sptr)
             evs[3 * c + 2].record(stream)
             assert st == rq.RQ_OK
@@ -540,6 +553,8 @@ def main():
             continue          # second-layer inputs come from the GPU's own GELU; skip
         xr = torch.from_numpy(xs_bits[rs].view(np.int16)).view(tdt).float().numpy().astype(np.float64)
         ref = xr @ g["W"][lin.name].astype(np.float64).T + g["bias"][lin.name].astype(np.float64)
+        if act_of[lin.name] != rq.RQ_ACT_NONE:
+            ref = synth.gelu(ref, "gelu_erf" if act_of[lin.name] == rq.RQ_ACT_GELU_ERF else "gelu_tanh")
         got = sets[0]["Y"][lin.name][torch.from_numpy(rs).to(dev)].float().cpu().numpy().astype(np.float64)
         qerr[lin.name] = round(float(np.linalg.norm(got - ref) / np.linalg.norm(ref)), 6)
 
@@ -550,7 +565,10 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "int4 codes as fp6 e2m3" if wl == rq.RQ_W_FP6 else "int8",
         "data": "synthetic",
         "config": {"workload": cfg.workload, "M": M, "K": cfg.K, "N": [l.N for l in cfg.linears],
-                   "io": cfg.io, "bits": bits, "calls_per_step": nl},
+                   "io": cfg.io, "bits": bits, "calls_per_step": nl,
+                   **({"gelu": "torch op between the linears" if args.unfused_gelu else
+                       "fused into the first linear's epilogue"}
+                      if any(l.source in gelu_act for l in cfg.linears) else {})},
         "int8_peak_frac": round(tops / PEAK_INT8_TOPS, 4),
         "roofline": roofline, "roofline_rotate_quant": roofline_rq, "calls": calls,
         "weight_quant_ms_offline": round(wq_ms, 3), "buffer_sets": R,

@@ -104,6 +104,19 @@ enum { RQ_W_ROWS = 0, RQ_W_FP6 = 1 };                   /* weight code layouts (
  *                 scale. The GEMM is unchanged: w_scale[n] is simply constant. */
 enum { RQ_W_ABSMAX = 0, RQ_W_MSE = 1, RQ_W_TENSOR = 2 };
 
+/* Activation fused into the epilogue, for the first linear of an MLP pair (the "SAM 3.1
+ * Multiplex INT8/INT4 ConvRot" page, "Future improvements": larger gains from fusing
+ * operations and cutting dispatches; the pages do not name the MLP's activation). With v the
+ * binary32 epilogue value fma(f32(acc), fl(s_w * s_x), bias), the stored value is
+ * round_to_nearest_even(GELU(v)) in fp16/bf16, GELU evaluated in binary32 with the device math
+ * library as
+ *   RQ_ACT_GELU_ERF   0.5 v erfc(-v / sqrt 2)                    (= v * Phi(v), the erf form)
+ *   RQ_ACT_GELU_TANH  v * logistic(2u), u = sqrt(2/pi) (v + 0.044715 v^3)   (the tanh form,
+ *                     0.5 v (1 + tanh u)), the logistic as 1/(1+e) or e/(1+e), e = exp(-2|u|)
+ * which is within a few binary32 ulps of the exact value: the output is the correctly rounded
+ * GELU except, rarely, one ulp away next to a rounding midpoint. RQ_ACT_NONE stores v itself. */
+enum { RQ_ACT_NONE = 0, RQ_ACT_GELU_ERF = 1, RQ_ACT_GELU_TANH = 2 };
+
 typedef struct {
   int32_t bits;       /* 8 (W8A8) or 4 (W4A4) */
   int32_t rot_kind;   /* must be RQ_ROT_WHT */
@@ -117,6 +130,10 @@ typedef struct {
                            rq_quantize_weights, rq_rotq_linear and the GEMM entry points. The
                            GEMM entry points need x_layout == RQ_X_FP6 exactly when w_layout is
                            RQ_W_FP6; rq_rotq_linear picks its workspace layout to match. */
+  int32_t act;          /* RQ_ACT_NONE, RQ_ACT_GELU_ERF or RQ_ACT_GELU_TANH: activation applied
+                           by the epilogue of rq_rotq_linear and rq_gemm_dequant to each fp32
+                           value before its fp16/bf16 rounding (below); ignored by the other
+                           entry points. */
 } rq_qconfig;
 
 /* Bytes of activation codes for `rows` rows of length K in cfg's bits and x_layout
@@ -159,7 +176,8 @@ size_t rq_rotq_linear_workspace_size(int64_t M, int64_t K, const rq_qconfig *cfg
  *   Wq        codes in cfg->w_layout (from rq_quantize_weights with the same cfg)
  *   w_scale   [N] float
  *   bias      [N] float, or NULL (no bias)
- *   Y         out: [M, N], same dtype as X; must not overlap X, Wq or the workspace
+ *   Y         out: [M, N], same dtype as X, after cfg->act; must not overlap X, Wq or the
+ *             workspace
  *   workspace device buffer of ws_bytes >= rq_rotq_linear_workspace_size(M, K, cfg) */
 rq_status rq_rotq_linear(const void *X, int32_t x_dtype, int64_t M, int64_t K,
                          const void *Wq, const float *w_scale, int64_t N, const float *bias,
@@ -169,7 +187,7 @@ rq_status rq_rotq_linear(const void *X, int32_t x_dtype, int64_t M, int64_t K,
 /* The GEMM + epilogue alone (the second kernel of rq_rotq_linear).
  *   Xq codes of M rows in cfg->x_layout (as rq_rotate_quantize writes them), x_scale [M];
  *   Wq, w_scale, bias as above;
- *   Y  out: [M, N] of y_dtype (RQ_F16 or RQ_BF16). */
+ *   Y  out: [M, N] of y_dtype (RQ_F16 or RQ_BF16), after cfg->act. */
 rq_status rq_gemm_dequant(const void *Xq, const float *x_scale, const void *Wq,
                           const float *w_scale, const float *bias, int64_t M, int64_t N,
                           int64_t K, const rq_qconfig *cfg, void *Y, int32_t y_dtype,

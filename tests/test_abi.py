@@ -156,6 +156,19 @@ def test_entry_points_reject_before_launch():
                                   A + 2 * GB, None) == rq.RQ_EUNSUPPORTED
     assert rq.rq_quantize_weights(A, rq.RQ_F32, 16, 128, rq.make_cfg(4, w_layout=2), A + GB,
                                   A + 2 * GB, None) == rq.RQ_EINVAL
+    # The epilogue activation is validated for every entry point (M == 0 launches nothing).
+    for act in (rq.RQ_ACT_NONE, rq.RQ_ACT_GELU_ERF, rq.RQ_ACT_GELU_TANH):
+        c = rq.make_cfg(8, act=act)
+        assert rq.rq_gemm_dequant(A, A + GB, A + 2 * GB, A + 3 * GB, None, 0, 32, 128, c, A + 4 * GB,
+                                  rq.RQ_F16, None) == rq.RQ_OK
+        assert rq.rq_check_rotq_linear_args(A, rq.RQ_F16, 16, 128, A + GB, A + 2 * GB, 32, None, c,
+                                            A + 3 * GB, A + 4 * GB, 1 << 20) == rq.RQ_OK
+    for act in (-1, 3):
+        c = rq.make_cfg(8, act=act)
+        assert rq.rq_gemm_dequant(A, A + GB, A + 2 * GB, A + 3 * GB, None, 16, 32, 128, c, A + 4 * GB,
+                                  rq.RQ_F16, None) == rq.RQ_EINVAL
+        assert rq.rq_check_rotq_linear_args(A, rq.RQ_F16, 16, 128, A + GB, A + 2 * GB, 32, None, c,
+                                            A + 3 * GB, A + 4 * GB, 1 << 20) == rq.RQ_EINVAL
     for mode in (rq.RQ_W_ABSMAX, rq.RQ_W_MSE, rq.RQ_W_TENSOR):
         c = rq.make_cfg(4, w_scale_mode=mode)
         assert rq.rq_quantize_weights(A, rq.RQ_F32, 0, 256, c, A + GB, A + 2 * GB, None) == rq.RQ_OK

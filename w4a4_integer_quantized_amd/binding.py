@@ -25,6 +25,7 @@ RQ_ROT_WHT = 1
 RQ_X_ROWS, RQ_X_TILED, RQ_X_FP6 = 0, 1, 2
 RQ_W_ROWS, RQ_W_FP6 = 0, 1
 RQ_W_ABSMAX, RQ_W_MSE, RQ_W_TENSOR = 0, 1, 2
+RQ_ACT_NONE, RQ_ACT_GELU_ERF, RQ_ACT_GELU_TANH = 0, 1, 2
 
 
 class ConvRotError(RuntimeError):
@@ -35,7 +36,8 @@ class ConvRotError(RuntimeError):
 
 class rq_qconfig(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int32), ("rot_kind", ctypes.c_int32), ("rot_block", ctypes.c_int32),
-                ("x_layout", ctypes.c_int32), ("w_scale_mode", ctypes.c_int32), ("w_layout", ctypes.c_int32)]
+                ("x_layout", ctypes.c_int32), ("w_scale_mode", ctypes.c_int32), ("w_layout", ctypes.c_int32),
+                ("act", ctypes.c_int32)]
 
 
 _lib = None
@@ -99,8 +101,8 @@ def _check(status: int, where: str):
 
 def make_cfg(bits: int = 8, rot_block: int = 128, rot_kind: int = RQ_ROT_WHT,
              x_layout: int = RQ_X_ROWS, w_scale_mode: int = RQ_W_ABSMAX,
-             w_layout: int = RQ_W_ROWS) -> rq_qconfig:
-    return rq_qconfig(bits, rot_kind, rot_block, x_layout, w_scale_mode, w_layout)
+             w_layout: int = RQ_W_ROWS, act: int = RQ_ACT_NONE) -> rq_qconfig:
+    return rq_qconfig(bits, rot_kind, rot_block, x_layout, w_scale_mode, w_layout, act)
 
 
 # ----------------------------------------------------------------------------- raw entry points
@@ -223,13 +225,14 @@ def rotate_quantize(X, bits: int = 8, rot: int = 128, stream=None, x_layout: int
 
 
 def rotq_linear(X, Wq, w_scale, bias=None, bits: int = 8, rot: int = 128, workspace=None,
-                out=None, stream=None, w_layout: int = RQ_W_ROWS):
-    """Y [M, N] = dequant(int GEMM(rotate+quantize(X), Wq)) + bias, in X's dtype; N = len(w_scale).
-    w_layout must be the layout Wq was quantized in (RQ_W_FP6: the FP6 matrix-core path)."""
+                out=None, stream=None, w_layout: int = RQ_W_ROWS, act: int = RQ_ACT_NONE):
+    """Y [M, N] = act(dequant(int GEMM(rotate+quantize(X), Wq)) + bias), in X's dtype;
+    N = len(w_scale). w_layout must be the layout Wq was quantized in (RQ_W_FP6: the FP6
+    matrix-core path); act is RQ_ACT_NONE, RQ_ACT_GELU_ERF or RQ_ACT_GELU_TANH."""
     torch = _torch()
     M, K = X.shape
     N = w_scale.shape[0]
-    cfg = make_cfg(bits, rot, w_layout=w_layout)
+    cfg = make_cfg(bits, rot, w_layout=w_layout, act=act)
     need = rq_rotq_linear_workspace_size(M, K, cfg)
     if workspace is None:
         workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=X.device)
@@ -242,9 +245,10 @@ def rotq_linear(X, Wq, w_scale, bias=None, bits: int = 8, rot: int = 128, worksp
 
 
 def gemm_dequant(Xq, x_scale, Wq, w_scale, bias=None, bits: int = 8, K: Optional[int] = None,
-                 out_dtype=None, stream=None, x_layout: int = RQ_X_ROWS, w_layout: int = RQ_W_ROWS):
-    """Y [M, N] from codes; M = len(x_scale), N = len(w_scale), K from Wq unless given (give K
-    for FP6 weight tiles)."""
+                 out_dtype=None, stream=None, x_layout: int = RQ_X_ROWS, w_layout: int = RQ_W_ROWS,
+                 act: int = RQ_ACT_NONE):
+    """Y [M, N] from codes, after the epilogue activation act; M = len(x_scale),
+    N = len(w_scale), K from Wq unless given (give K for FP6 weight tiles)."""
     torch = _torch()
     M = x_scale.shape[0]
     N = w_scale.shape[0]
@@ -253,7 +257,7 @@ def gemm_dequant(Xq, x_scale, Wq, w_scale, bias=None, bits: int = 8, K: Optional
     Y = torch.empty((M, N), dtype=out_dtype, device=Xq.device)
     _check(rq_gemm_dequant(_dev(Xq, "Xq"), _dev(x_scale, "x_scale"), _dev(Wq, "Wq"), _dev(w_scale, "w_scale"),
                            _dev(bias, "bias") if bias is not None else None, M, N, K,
-                           make_cfg(bits, x_layout=x_layout, w_layout=w_layout), Y.data_ptr(), _dtype_code(Y),
+                           make_cfg(bits, x_layout=x_layout, w_layout=w_layout, act=act), Y.data_ptr(), _dtype_code(Y),
                            _stream(stream)), "rq_gemm_dequant")
     return Y
 

@@ -88,6 +88,8 @@ rq_status check_cfg(const rq_qconfig* cfg) {
       cfg->w_scale_mode != RQ_W_TENSOR)
     return fail(RQ_EINVAL, "w_scale_mode = %d (RQ_W_ABSMAX, RQ_W_MSE or RQ_W_TENSOR)",
                 cfg->w_scale_mode);
+  if (cfg->act != RQ_ACT_NONE && cfg->act != RQ_ACT_GELU_ERF && cfg->act != RQ_ACT_GELU_TANH)
+    return fail(RQ_EINVAL, "act = %d (RQ_ACT_NONE, RQ_ACT_GELU_ERF or RQ_ACT_GELU_TANH)", cfg->act);
   return ok();
 }
 
@@ -276,10 +278,11 @@ rq_status rq_rotq_linear(const void* X, int32_t x_dtype, int64_t M, int64_t K, c
                     "rotate_quant launch")))
     return s;
   if (xl == RQ_X_FP6)
-    return from_hip(convrot::launch_gemm_fp6(Xq, sx, Wq, w_scale, bias, M, N, K, Y, x_dtype, nullptr, st),
+    return from_hip(convrot::launch_gemm_fp6(Xq, sx, Wq, w_scale, bias, M, N, K, Y, x_dtype, nullptr,
+                                             cfg->act, st),
                     "gemm launch");
   return from_hip(convrot::launch_gemm(Xq, sx, Wq, w_scale, bias, M, N, K, cfg->bits, true, Y,
-                                       x_dtype, nullptr, st),
+                                       x_dtype, nullptr, cfg->act, st),
                   "gemm launch");
 }
 
@@ -293,10 +296,10 @@ rq_status rq_gemm_dequant(const void* Xq, const float* x_scale, const void* Wq,
   if (s || M == 0) return s;
   if (cfg->x_layout == RQ_X_FP6)
     return from_hip(convrot::launch_gemm_fp6(Xq, x_scale, Wq, w_scale, bias, M, N, K, Y, y_dtype, nullptr,
-                                             static_cast<hipStream_t>(stream)),
+                                             cfg->act, static_cast<hipStream_t>(stream)),
                     "gemm launch");
   return from_hip(convrot::launch_gemm(Xq, x_scale, Wq, w_scale, bias, M, N, K, cfg->bits,
-                                       cfg->x_layout == RQ_X_TILED, Y, y_dtype, nullptr,
+                                       cfg->x_layout == RQ_X_TILED, Y, y_dtype, nullptr, cfg->act,
                                        static_cast<hipStream_t>(stream)),
                   "gemm launch");
 }
@@ -307,10 +310,10 @@ rq_status rq_gemm_s32(const void* Xq, const void* Wq, int64_t M, int64_t N, int6
   if (s || M == 0) return s;
   if (cfg->x_layout == RQ_X_FP6)
     return from_hip(convrot::launch_gemm_fp6(Xq, nullptr, Wq, nullptr, nullptr, M, N, K, acc, RQ_F16, acc,
-                                             static_cast<hipStream_t>(stream)),
+                                             RQ_ACT_NONE, static_cast<hipStream_t>(stream)),
                     "gemm launch");
   return from_hip(convrot::launch_gemm(Xq, nullptr, Wq, nullptr, nullptr, M, N, K, cfg->bits,
-                                       cfg->x_layout == RQ_X_TILED, acc, RQ_F16, acc,
+                                       cfg->x_layout == RQ_X_TILED, acc, RQ_F16, acc, RQ_ACT_NONE,
                                        static_cast<hipStream_t>(stream)),
                   "gemm launch");
 }

@@ -34,6 +34,55 @@ __device__ __forceinline__ uint32_t pack2(float a, float b, int out) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// The MLP activation applied to the binary32 pre-activation v before the fp16/bf16 rounding
+// (act 0: none; 1: GELU, erf form; 2: GELU, tanh form), with the native v_exp_f32 (2^x) and
+// v_rcp_f32 (1/x), each within about 1 ulp, so that the epilogue's extra VALU work stays small:
+//  * erf form: x Phi(x) = 0.5 x erfc(-x / sqrt 2), erfc by the Chebyshev-fitted form of Press et
+//    al., Numerical Recipes, section 6.2 ("erfcc"): for z = |y|, t = 1 / (1 + z/2),
+//    erfc(z) = t exp(-z^2 + P(t)) with a degree-9 polynomial P (fractional error below 1.2e-7),
+//    and erfc(-z) = 2 - erfc(z).
+//  * tanh form: 0.5 x (1 + tanh u) = x logistic(2u), u = sqrt(2/pi) (x + 0.044715 x^3), the
+//    logistic taken as 1 / (1 + e) or e / (1 + e) with e = exp(-2|u|) <= 1, which never
+//    overflows.
+// Neither form cancels for negative x, so the relative error is a few binary32 ulps plus the
+// rounding of the exponent's argument, amplified as the tail steepens (about z^2 and 2|u|
+// ulps); the rounded output can differ from the correctly rounded one only next to a rounding
+// midpoint. Results below the binary32 normal range may come out as zero.
+enum ActKind { kActNone = 0, kActGeluErf = 1, kActGeluTanh = 2 };
+
+template <int ACT>
+__device__ __forceinline__ float activate(float v) {
+  constexpr float kLog2e = 1.44269504088896341f;
+  if constexpr (ACT == kActGeluErf) {
+    const float z = fabsf(v) * 0.707106781186547524f;          // |y|, y = -v / sqrt 2
+    const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.5f, z, 1.0f));
+    float p = 0.17087277f;
+    p = __builtin_fmaf(p, t, -0.82215223f);
+    p = __builtin_fmaf(p, t, 1.48851587f);
+    p = __builtin_fmaf(p, t, -1.13520398f);
+    p = __builtin_fmaf(p, t, 0.27886807f);
+    p = __builtin_fmaf(p, t, -0.18628806f);
+    p = __builtin_fmaf(p, t, 0.09678418f);
+    p = __builtin_fmaf(p, t, 0.37409196f);
+    p = __builtin_fmaf(p, t, 1.00002368f);
+    p = __builtin_fmaf(p, t, -1.26551223f);
+    // 2^32 * exp(-z^2 + P): scaled so that no intermediate leaves the binary32 normal range
+    // while the result is inside it (the native exp2 flushes subnormal results).
+    const float e32 = __builtin_amdgcn_exp2f(__builtin_fmaf(__builtin_fmaf(-z, z, p), kLog2e, 32.0f));
+    if (v <= 0.0f) return (0.5f * 0x1p-32f * v * t) * e32;           // 0.5 v erfc(|y|)
+    return (0.5f * v) * (2.0f - t * (0x1p-32f * e32));                // 0.5 v (2 - erfc(|y|))
+  } else if constexpr (ACT == kActGeluTanh) {
+    const float m = v * __builtin_fmaf(0.044715f, v * v, 1.0f);       // v + 0.044715 v^3
+    // e = exp(-2|u|) = 2^(-2 sqrt(2/pi) log2(e) |m|), computed as 2^32 e (see above)
+    const float e32 = __builtin_amdgcn_exp2f(__builtin_fmaf(-2.30220819814432500f, fabsf(m), 32.0f));
+    const float r = __builtin_amdgcn_rcpf(__builtin_fmaf(0x1p-32f, e32, 1.0f));
+    if (m >= 0.0f) return v * r;
+    return ((0x1p-32f * v) * e32) * r;
+  } else {
+    return v;
+  }
+}
+
 // The tile's epilogue for NB consecutive 32-row blocks of this wave: acc[a][b] holds the
 // 32 x 32 accumulator block of W rows a*32.. and tile rows row0 + b*32... Lane l holds
 // D[n][m] for m = b*32 + l%32 and n = a*32 + 8*(r/4) + 4*(l/32) + r%4, r = 0..15. Either raw
@@ -52,7 +101,7 @@ __device__ __forceinline__ float acc_float(const v16i& blk, int r) { return stat
 template <int BITS>
 __device__ __forceinline__ float acc_float(const v16f& blk, int r) { return blk[r]; }
 
-template <int BITS, int OUT, int NB, typename AccBlk>
+template <int BITS, int OUT, int NB, int ACT, typename AccBlk>
 __device__ __forceinline__ void tile_epilogue(AccBlk (&acc)[4][NB], const float* scales, uint8_t* stage,
                                               int row0, int lane, int m0, int n0, int M, int N,
                                               void* __restrict__ Y) {
@@ -100,7 +149,8 @@ __device__ __forceinline__ void tile_epilogue(AccBlk (&acc)[4][NB], const float*
           float y[4];
 #pragma unroll
           for (int e = 0; e < 4; e++) {
-            y[e] = __builtin_fmaf(acc_float<BITS>(acc[a][b], 4 * g + e), __fmul_rn(ws[e], xs[b]), bs[e]);
+            y[e] = activate<ACT>(
+                __builtin_fmaf(acc_float<BITS>(acc[a][b], 4 * g + e), __fmul_rn(ws[e], xs[b]), bs[e]));
           }
           uint2 o;
           o.x = pack2(y[0], y[1], OUT);
@@ -134,10 +184,35 @@ __device__ __forceinline__ void tile_epilogue(AccBlk (&acc)[4][NB], const float*
       const int n = n0 + 8 * ((lane & 15) ^ (row & 15));
       if (m < M && n < N) {
         // Streaming store: Y is written once and not re-read here, so it should not evict
-        // the Wq / Xq panels that neighbouring tiles re-read from L2.
+        // the Wq / Xq panels that neighbouring tiles re-read from L2. An activated output is
+        // the next linear's input, read right away: it is stored normally, so that it can
+        // still be in the Infinity Cache when the next rotate + quantize reads it.
         v4i* dst = reinterpret_cast<v4i*>(static_cast<uint16_t*>(Y) + (int64_t)m * N + n);
-        __builtin_nontemporal_store(__builtin_bit_cast(v4i, v[it]), dst);
+        if constexpr (ACT == kActNone) {
+          __builtin_nontemporal_store(__builtin_bit_cast(v4i, v[it]), dst);
+        } else {
+          *dst = __builtin_bit_cast(v4i, v[it]);
+        }
       }
+    }
+  }
+}
+
+// tile_epilogue with the launch's activation: one uniform branch per tile, so the variant
+// without an activation carries no activation code.
+template <int BITS, int OUT, int NB, typename AccBlk>
+__device__ __forceinline__ void tile_epilogue_act(int act, AccBlk (&acc)[4][NB], const float* scales,
+                                                  uint8_t* stage, int row0, int lane, int m0, int n0,
+                                                  int M, int N, void* __restrict__ Y) {
+  if constexpr (OUT == kOutS32) {
+    tile_epilogue<BITS, OUT, NB, kActNone>(acc, scales, stage, row0, lane, m0, n0, M, N, Y);
+  } else {
+    if (act == kActNone) {
+      tile_epilogue<BITS, OUT, NB, kActNone>(acc, scales, stage, row0, lane, m0, n0, M, N, Y);
+    } else if (act == kActGeluErf) {
+      tile_epilogue<BITS, OUT, NB, kActGeluErf>(acc, scales, stage, row0, lane, m0, n0, M, N, Y);
+    } else {
+      tile_epilogue<BITS, OUT, NB, kActGeluTanh>(acc, scales, stage, row0, lane, m0, n0, M, N, Y);
     }
   }
 }

@@ -86,7 +86,7 @@ template <int OUT, int SPLIT>
 __global__ __launch_bounds__(kThreads6 * SPLIT, 2 / SPLIT) void gemm_fp6_kernel(
     const uint8_t* __restrict__ Xt, const float* __restrict__ sx, const uint8_t* __restrict__ Wt,
     const float* __restrict__ sw, const float* __restrict__ bias, void* __restrict__ Y, int M,
-    int N, int K, int tiles_m, int tiles_n) {
+    int N, int K, int tiles_m, int tiles_n, int act) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[lds_bytes6<SPLIT>()];
   constexpr int kSlot = SPLIT * kStage6;                 // one ring stage, all groups
   constexpr int kScales = lds_bytes6<SPLIT>() - (2 * kBN + kBM) * 4;
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(kThreads6 * SPLIT, 2 / SPLIT) void gemm_fp6_kernel(
 
   const float* scales = reinterpret_cast<const float*>(lds + kScales);
   if constexpr (SPLIT == 1) {
-    tile_epilogue<4, OUT, 2>(acc, scales, lds + wave * (64 * 256), wave * 64, lane, m0, n0, M, N, Y);
+    tile_epilogue_act<4, OUT, 2>(act, acc, scales, lds + wave * (64 * 256), wave * 64, lane, m0, n0, M, N, Y);
   } else {
     // Group g finishes row block b = g: it sends its partial sums of block 1 - g to the partner
     // wave (wave_all ^ 4) and adds the partner's partials of block g (exact: integers < 2^24).
@@ -270,7 +270,7 @@ __global__ __launch_bounds__(kThreads6 * SPLIT, 2 / SPLIT) void gemm_fp6_kernel(
           keep[a][0][4 * r4 + 3] = acc[a][KB][4 * r4 + 3] + o.w;
         }
       __syncthreads();   // every exchange read is done before the staging below reuses LDS
-      tile_epilogue<4, OUT, 1>(keep, scales, lds + wave_all * (32 * 256), wave * 64 + KB * 32, lane,
+      tile_epilogue_act<4, OUT, 1>(act, keep, scales, lds + wave_all * (32 * 256), wave * 64 + KB * 32, lane,
                                m0, n0, M, N, Y);
     };
     if (grp == 0) {
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(kThreads6 * SPLIT, 2 / SPLIT) void gemm_fp6_kernel(
 
 template <int OUT>
 hipError_t launch6(const void* Xt, const float* sx, const void* Wt, const float* sw,
-                   const float* bias, int64_t M, int64_t N, int64_t K, void* Y, hipStream_t st) {
+                   const float* bias, int64_t M, int64_t N, int64_t K, void* Y, int act, hipStream_t st) {
   const int tiles_m = (int)((M + kBM - 1) / kBM);
   const int tiles_n = (int)((N + kBN - 1) / kBN);
   const int ntiles = tiles_m * tiles_n;
@@ -292,11 +292,11 @@ hipError_t launch6(const void* Xt, const float* sx, const void* Wt, const float*
   if (ntiles <= kNumCUs && nsl % 2 == 0 && nsl >= 16) {
     hipLaunchKernelGGL((gemm_fp6_kernel<OUT, 2>), dim3(grid), dim3(2 * kThreads6), 0, st,
                        static_cast<const uint8_t*>(Xt), sx, static_cast<const uint8_t*>(Wt), sw,
-                       bias, Y, (int)M, (int)N, (int)K, tiles_m, tiles_n);
+                       bias, Y, (int)M, (int)N, (int)K, tiles_m, tiles_n, act);
   } else {
     hipLaunchKernelGGL((gemm_fp6_kernel<OUT, 1>), dim3(grid), dim3(kThreads6), 0, st,
                        static_cast<const uint8_t*>(Xt), sx, static_cast<const uint8_t*>(Wt), sw,
-                       bias, Y, (int)M, (int)N, (int)K, tiles_m, tiles_n);
+                       bias, Y, (int)M, (int)N, (int)K, tiles_m, tiles_n, act);
   }
   return hipGetLastError();
 }
@@ -305,11 +305,11 @@ hipError_t launch6(const void* Xt, const float* sx, const void* Wt, const float*
 
 hipError_t launch_gemm_fp6(const void* Xt, const float* sx, const void* Wt, const float* sw,
                            const float* bias, int64_t M, int64_t N, int64_t K, void* Y,
-                           int out_dt, int32_t* acc32, hipStream_t stream) {
+                           int out_dt, int32_t* acc32, int act, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
-  if (acc32) return launch6<kOutS32>(Xt, sx, Wt, sw, bias, M, N, K, acc32, stream);
-  if (out_dt == kF16) return launch6<kOutF16>(Xt, sx, Wt, sw, bias, M, N, K, Y, stream);
-  return launch6<kOutBF16>(Xt, sx, Wt, sw, bias, M, N, K, Y, stream);
+  if (acc32) return launch6<kOutS32>(Xt, sx, Wt, sw, bias, M, N, K, acc32, kActNone, stream);
+  if (out_dt == kF16) return launch6<kOutF16>(Xt, sx, Wt, sw, bias, M, N, K, Y, act, stream);
+  return launch6<kOutBF16>(Xt, sx, Wt, sw, bias, M, N, K, Y, act, stream);
 }
 
 }  // namespace convrot

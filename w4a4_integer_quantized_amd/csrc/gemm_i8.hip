@@ -97,7 +97,7 @@ template <int BITS, int OUT, bool XT, int SPLIT>
 __global__ __launch_bounds__(kThreads * SPLIT, 2 / SPLIT) void gemm_kernel(
     const uint8_t* __restrict__ Xq, const float* __restrict__ sx, const uint8_t* __restrict__ Wq,
     const float* __restrict__ sw, const float* __restrict__ bias, void* __restrict__ Y, int M,
-    int N, int Kb, int tiles_m, int tiles_n) {
+    int N, int Kb, int tiles_m, int tiles_n, int act) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[lds_bytes<SPLIT>()];
   constexpr int kRing = kStages * SPLIT * kStageBytes;   // also where the scales are parked
   constexpr int kSlot = SPLIT * kStageBytes;              // one ring stage, all groups
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(kThreads * SPLIT, 2 / SPLIT) void gemm_kernel(
 
   const float* scales = reinterpret_cast<const float*>(lds + kRing);
   if constexpr (SPLIT == 1) {
-    tile_epilogue<BITS, OUT, 2>(acc, scales, lds + wave * (64 * 256), wave * 64, lane, m0, n0, M, N, Y);
+    tile_epilogue_act<BITS, OUT, 2>(act, acc, scales, lds + wave * (64 * 256), wave * 64, lane, m0, n0, M, N, Y);
   } else {
     // Group g finishes row block b = g of its four waves' rows: it sends its partial sums of
     // block 1 - g to the partner wave (wave_all ^ 4) and adds the partner's partials of block g.
@@ -318,7 +318,7 @@ __global__ __launch_bounds__(kThreads * SPLIT, 2 / SPLIT) void gemm_kernel(
           keep[a][0][4 * r4 + 3] = acc[a][KB][4 * r4 + 3] + o.w;
         }
       __syncthreads();   // every exchange read is done before the staging below reuses LDS
-      tile_epilogue<BITS, OUT, 1>(keep, scales, lds + wave_all * (32 * 256), wave * 64 + KB * 32, lane,
+      tile_epilogue_act<BITS, OUT, 1>(act, keep, scales, lds + wave_all * (32 * 256), wave * 64 + KB * 32, lane,
                                   m0, n0, M, N, Y);
     };
     if (grp == 0) {
@@ -342,7 +342,7 @@ template <int BITS, int OUT, bool XT>
 __global__ __launch_bounds__(512, 1) void gemm_n2_kernel(
     const uint8_t* __restrict__ Xq, const float* __restrict__ sx, const uint8_t* __restrict__ Wq,
     const float* __restrict__ sw, const float* __restrict__ bias, void* __restrict__ Y, int M,
-    int N, int Kb, int tiles_m, int tiles_n) {
+    int N, int Kb, int tiles_m, int tiles_n, int act) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsN2];
   constexpr int kScales = kLdsN2 - 2 * kScaleBlk;
 
@@ -516,12 +516,12 @@ __global__ __launch_bounds__(512, 1) void gemm_n2_kernel(
   body(std::false_type{}, std::false_type{}, kt, wf0, xf0);
   __syncthreads();
   const float* scales = reinterpret_cast<const float*>(lds + kScales + grp * kScaleBlk);
-  tile_epilogue<BITS, OUT, 2>(acc, scales, lds + wave_all * (64 * 256), wave * 64, lane, m0, n0 + 128 * grp, M, N, Y);
+  tile_epilogue_act<BITS, OUT, 2>(act, acc, scales, lds + wave_all * (64 * 256), wave * 64, lane, m0, n0 + 128 * grp, M, N, Y);
 }
 
 template <int BITS, int OUT, bool XT>
 hipError_t launch(const void* Xq, const float* sx, const void* Wq, const float* sw,
-                  const float* bias, int64_t M, int64_t N, int64_t Kb, void* Y, hipStream_t st) {
+                  const float* bias, int64_t M, int64_t N, int64_t Kb, void* Y, int act, hipStream_t st) {
   const int tiles_m = (int)((M + kBM - 1) / kBM);
   const int tiles_n = (int)((N + kBN - 1) / kBN);
   const int ntiles = tiles_m * tiles_n;
@@ -536,17 +536,17 @@ hipError_t launch(const void* Xq, const float* sx, const void* Wq, const float* 
   if (ntiles <= kNumCUs && (Kb / kBKB) % 2 == 0 && Kb / kBKB >= 16) {
     hipLaunchKernelGGL((gemm_kernel<BITS, OUT, XT, 2>), dim3(grid), dim3(2 * kThreads), 0, st,
                        static_cast<const uint8_t*>(Xq), sx, static_cast<const uint8_t*>(Wq), sw,
-                       bias, Y, (int)M, (int)N, (int)Kb, tiles_m, tiles_n);
+                       bias, Y, (int)M, (int)N, (int)Kb, tiles_m, tiles_n, act);
   } else if (ntiles > kNumCUs && Kb >= 3072) {
     const int tiles_n2 = (int)((N + 255) / 256);
     const int ntiles2 = tiles_m * tiles_n2;
     hipLaunchKernelGGL((gemm_n2_kernel<BITS, OUT, XT>), dim3(((ntiles2 + 7) / 8) * 8), dim3(512), 0,
                        st, static_cast<const uint8_t*>(Xq), sx, static_cast<const uint8_t*>(Wq), sw,
-                       bias, Y, (int)M, (int)N, (int)Kb, tiles_m, tiles_n2);
+                       bias, Y, (int)M, (int)N, (int)Kb, tiles_m, tiles_n2, act);
   } else {
     hipLaunchKernelGGL((gemm_kernel<BITS, OUT, XT, 1>), dim3(grid), dim3(kThreads), 0, st,
                        static_cast<const uint8_t*>(Xq), sx, static_cast<const uint8_t*>(Wq), sw,
-                       bias, Y, (int)M, (int)N, (int)Kb, tiles_m, tiles_n);
+                       bias, Y, (int)M, (int)N, (int)Kb, tiles_m, tiles_n, act);
   }
   return hipGetLastError();
 }
@@ -554,23 +554,24 @@ hipError_t launch(const void* Xq, const float* sx, const void* Wq, const float* 
 template <bool XT>
 hipError_t launch_layout(const void* Xq, const float* sx, const void* Wq, const float* sw,
                          const float* bias, int64_t M, int64_t N, int64_t Kb, int bits, void* Y,
-                         int out_dt, int32_t* acc32, hipStream_t stream) {
+                         int out_dt, int32_t* acc32, int act, hipStream_t stream) {
   if (acc32) {
-    return bits == 8 ? launch<8, kOutS32, XT>(Xq, sx, Wq, sw, bias, M, N, Kb, acc32, stream)
-                     : launch<4, kOutS32, XT>(Xq, sx, Wq, sw, bias, M, N, Kb, acc32, stream);
+    return bits == 8 ? launch<8, kOutS32, XT>(Xq, sx, Wq, sw, bias, M, N, Kb, acc32, act, stream)
+                     : launch<4, kOutS32, XT>(Xq, sx, Wq, sw, bias, M, N, Kb, acc32, act, stream);
   }
   if (out_dt == kF16)
-    return bits == 8 ? launch<8, kOutF16, XT>(Xq, sx, Wq, sw, bias, M, N, Kb, Y, stream)
-                     : launch<4, kOutF16, XT>(Xq, sx, Wq, sw, bias, M, N, Kb, Y, stream);
-  return bits == 8 ? launch<8, kOutBF16, XT>(Xq, sx, Wq, sw, bias, M, N, Kb, Y, stream)
-                   : launch<4, kOutBF16, XT>(Xq, sx, Wq, sw, bias, M, N, Kb, Y, stream);
+    return bits == 8 ? launch<8, kOutF16, XT>(Xq, sx, Wq, sw, bias, M, N, Kb, Y, act, stream)
+                     : launch<4, kOutF16, XT>(Xq, sx, Wq, sw, bias, M, N, Kb, Y, act, stream);
+  return bits == 8 ? launch<8, kOutBF16, XT>(Xq, sx, Wq, sw, bias, M, N, Kb, Y, act, stream)
+                   : launch<4, kOutBF16, XT>(Xq, sx, Wq, sw, bias, M, N, Kb, Y, act, stream);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const void* Xq, const float* sx, const void* Wq, const float* sw,
                        const float* bias, int64_t M, int64_t N, int64_t K, int bits,
-                       bool x_tiled, void* Y, int out_dt, int32_t* acc32, hipStream_t stream) {
+                       bool x_tiled, void* Y, int out_dt, int32_t* acc32, int act,
+                       hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   const int64_t Kb = bits == 8 ? K : K / 2;
   // Tiled activation codes (the fused path): these kernels measured fastest on every workload
@@ -578,12 +579,13 @@ hipError_t launch_gemm(const void* Xq, const float* sx, const void* Wq, const fl
   // enough tiles to fill the machine, where the 128-byte-row 256 x 256 kernel's lower operand
   // traffic per MFMA measured faster (by up to ~20%) than 64-byte row segments; from 3072 bytes
   // on, the eight-wave 256 x 256 kernel here measured faster still (by ~15%).
+  // The 128-byte-row kernel has no activation variant; with one, the 64-byte-row kernels run.
   if (x_tiled)
-    return launch_layout<true>(Xq, sx, Wq, sw, bias, M, N, Kb, bits, Y, out_dt, acc32, stream);
+    return launch_layout<true>(Xq, sx, Wq, sw, bias, M, N, Kb, bits, Y, out_dt, acc32, act, stream);
   const int64_t wide_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  if (wide_gemm_supported(Kb) && Kb >= 1536 && Kb < 3072 && wide_tiles >= 192)
+  if (act == kActNone && wide_gemm_supported(Kb) && Kb >= 1536 && Kb < 3072 && wide_tiles >= 192)
     return launch_gemm_wide(Xq, sx, Wq, sw, bias, M, N, K, bits, Y, out_dt, acc32, stream);
-  return launch_layout<false>(Xq, sx, Wq, sw, bias, M, N, Kb, bits, Y, out_dt, acc32, stream);
+  return launch_layout<false>(Xq, sx, Wq, sw, bias, M, N, Kb, bits, Y, out_dt, acc32, act, stream);
 }
 
 }  // namespace convrot

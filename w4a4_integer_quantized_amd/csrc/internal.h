@@ -28,17 +28,19 @@ hipError_t launch_weight_quant(int mode, const void* W, int dt, int64_t N, int64
                                bool fp6, void* Wq, float* S, hipStream_t stream);
 
 // acc = Xq * Wq^T over K (codes of `bits` bits; Xq row-major or tiled when x_tiled, Wq
-// row-major), then either the dequantizing epilogue into Y (out_dt kF16 / kBF16) or, when
-// acc32 != nullptr, the raw int32 accumulators.
+// row-major), then either the dequantizing epilogue into Y (out_dt kF16 / kBF16), with the
+// activation `act` (gemm::ActKind) applied before the rounding, or, when acc32 != nullptr, the
+// raw int32 accumulators (act ignored).
 hipError_t launch_gemm(const void* Xq, const float* sx, const void* Wq, const float* sw,
                        const float* bias, int64_t M, int64_t N, int64_t K, int bits,
-                       bool x_tiled, void* Y, int out_dt, int32_t* acc32, hipStream_t stream);
+                       bool x_tiled, void* Y, int out_dt, int32_t* acc32, int act,
+                       hipStream_t stream);
 
 // 4-bit codes on the FP6 matrix cores: Xt and Wt in the FP6 tile layout of convrot.h (256-row
-// and 128-row panels). K % 128 == 0.
+// and 128-row panels). K % 128 == 0. `act` as for launch_gemm.
 hipError_t launch_gemm_fp6(const void* Xt, const float* sx, const void* Wt, const float* sw,
                            const float* bias, int64_t M, int64_t N, int64_t K, void* Y,
-                           int out_dt, int32_t* acc32, hipStream_t stream);
+                           int out_dt, int32_t* acc32, int act, hipStream_t stream);
 
 // The same GEMM on 256 x 256 tiles with 128-byte k steps (launch_gemm picks it for long K);
 // it needs Kb (K in bytes of codes) to be a multiple of 128 and at least 256.

@@ -106,6 +106,11 @@ def to_io_bits(x: np.ndarray, io: str) -> np.ndarray:
     raise ValueError(io)
 
 
+def gelu(z: np.ndarray, kind: str) -> np.ndarray:
+    """GELU in float64 (erf or tanh form), for making second-layer inputs and error context."""
+    return _gelu(z, kind)
+
+
 def _gelu(z: np.ndarray, kind: str) -> np.ndarray:
     z = z.astype(np.float64)
     if kind == "gelu_erf":
