@@ -309,7 +309,7 @@ def rotq_linear(X: np.ndarray, x_dtype: int, W_codes: np.ndarray, w_scale: np.nd
     """Online step on X bits [M, K] against already quantized weights.
 
     Returns dict with x_codes, x_scale, acc, Y (uint16 bits in X's dtype) and, with an
-    activation, g64 (its binary64 value before rounding).
+    activation, g64 (its binary64 value before rounding) and v (the fp32 pre-activation).
     """
     xc, xs, _ = quantize_rows(X, x_dtype, bits, rotate)
     acc = gemm_s32(xc, W_codes)
@@ -318,6 +318,7 @@ def rotq_linear(X: np.ndarray, x_dtype: int, W_codes: np.ndarray, w_scale: np.nd
         out["Y"] = epilogue(acc, xs, w_scale, bias, x_dtype)
     else:
         out["Y"], out["g64"] = epilogue_act(acc, xs, w_scale, bias, x_dtype, act)
+        out["v"] = epilogue_act(acc, xs, w_scale, bias, x_dtype, ACT_NONE)[1]
     return out
 
 
