@@ -193,11 +193,14 @@ def pmc_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     print(json.dumps(doc))
 
 
-def cpu_baseline(g, cfg, target_s):
-    """The CPU oracle as it stands on a bounded sample of the same workload's rows."""
+def cpu_baseline(g, cfg, target_s, act_of=None):
+    """The CPU oracle as it stands on a bounded sample of the same workload's rows (with the
+    fused activation where the GPU step has one), on all host cores, then single-threaded on a
+    smaller sample."""
     import numpy as np
     import oracle
     dt = oracle.F16 if cfg.io == "f16" else oracle.BF16
+    act_of = act_of or {}
     wq = {lin.name: oracle.quantize_weights(g["W"][lin.name], cfg.bits)[0::2] for lin in cfg.linears}
 
     split = {"rq_s": 0.0, "rq_bytes": 0, "gemm_s": 0.0, "gemm_ops": 0}
@@ -213,7 +216,11 @@ def cpu_baseline(g, cfg, target_s):
             xc, xs, _ = oracle.quantize_rows(src, dt, cfg.bits)
             t2 = time.perf_counter()
             acc = oracle.gemm_s32(xc, wc)
-            oracle.epilogue(acc, xs, ws, g["bias"][lin.name], dt)
+            act = act_of.get(lin.name, 0)
+            if act:
+                oracle.epilogue_act(acc, xs, ws, g["bias"][lin.name], dt, act)
+            else:
+                oracle.epilogue(acc, xs, ws, g["bias"][lin.name], dt)
             t3 = time.perf_counter()
             split["rq_s"] += t2 - t1
             split["rq_bytes"] += rows * lin.K * 2 + rows * lin.K * cfg.bits // 8 + 4 * rows
@@ -236,12 +243,24 @@ def cpu_baseline(g, cfg, target_s):
         total_t += t
         total_ops += ops
         passes += 1
-    return {"value": total_ops / total_t / 1e12, "unit": "TOPS", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "rotate_quant_GBps": round(split["rq_bytes"] / split["rq_s"] / 1e9, 3),
-            "gemm_epilogue_TOPS": round(split["gemm_ops"] / split["gemm_s"] / 1e12, 5),
-            "sample": "first %d of %d tokens, every linear of the step (rotate+quantize, int GEMM, "
-                      "epilogue), %d passes, %.1f s" % (rows, cfg.M, passes, total_t)}
+    out = {"value": total_ops / total_t / 1e12, "unit": "TOPS", "cores": oracle.num_threads(),
+           "kind": "oracle",
+           "rotate_quant_GBps": round(split["rq_bytes"] / split["rq_s"] / 1e9, 3),
+           "gemm_epilogue_TOPS": round(split["gemm_ops"] / split["gemm_s"] / 1e12, 5),
+           "sample": "first %d of %d tokens, every linear of the step (rotate+quantize, int GEMM, "
+                     "epilogue%s), %d passes, %.1f s" % (rows, cfg.M, " with the fused GELU" if any(act_of.values())
+                                                          else "", passes, total_t)}
+    # One single-threaded pass on a smaller sample (about a fifth of the target time).
+    cores = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        rows1 = max(1, min(rows, int(rows * 0.2 * target_s / max(total_t / passes * cores, 1e-6))))
+        t1, ops1 = run(rows1)
+    finally:
+        oracle.set_num_threads(cores)
+    out["single_thread"] = {"value": ops1 / t1 / 1e12, "unit": "TOPS", "cores": 1,
+                            "sample": "first %d tokens, one pass, %.1f s" % (rows1, t1)}
+    return out
 
 
 def offline_weight_quant(rq, torch, W_np, bits, dev, reps=5):
@@ -581,7 +600,7 @@ def main():
     out["weight_quantizer"] = offline_weight_quant(rq, torch, g["W"][dom.name], bits, dev)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle, ~%.0f s)" % args.cpu_seconds)
-        out["cpu_baseline"] = cpu_baseline(g, cfg, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(g, cfg, args.cpu_seconds, act_of)
     print(json.dumps(out))
 
 

@@ -57,6 +57,7 @@ def _load():
         lib.orc_hadamard_entry.argtypes = [I, I]
         lib.orc_hadamard_entry.restype = I
         lib.orc_num_threads.restype = I
+        lib.orc_set_num_threads.argtypes = [I]
         lib.orc_quantize_rows_mse.argtypes = [P, I, I64, I64, I, P, P, P, P]
         lib.orc_quantize_rows_mse.restype = I
         lib.orc_quantize_tensorwise.argtypes = [P, I, I64, I64, I, P, P, P]
@@ -73,6 +74,11 @@ def _ptr(a: np.ndarray):
 
 def num_threads() -> int:
     return _load().orc_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads the oracle's OpenMP loops use from now on (timing runs only)."""
+    _load().orc_set_num_threads(int(n))
 
 
 # ---------------------------------------------------------------------------- formats

@@ -420,6 +420,14 @@ void orc_bf16_to_f32_array(const uint16_t *x, int64_t n, float *y) {
 void orc_fwht128_rows(float *v, int64_t nblocks) {
   for (int64_t b = 0; b < nblocks; b++) orc_fwht128(v + b * ORC_BLOCK);
 }
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+  extern void omp_set_num_threads(int);
+  omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
 int orc_num_threads(void) {
 #ifdef _OPENMP
   extern int omp_get_max_threads(void);
