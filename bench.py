@@ -139,11 +139,13 @@ def _median_by_group(csv_path, counter, select):
     return {k: (float(np.median(v)), len(v)) for k, v in groups.items()}
 
 
-def pmc_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+def pmc_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, out_path=None):
     """Reduce four rocprofv3 --pmc runs (bench FETCH_SIZE, bench WRITE_SIZE, copy FETCH_SIZE,
     copy WRITE_SIZE; counters in KiB per dispatch) to bytes per launch of the dominant GEMM and
     of the rotate+quantize kernel, scaled by what the same counters read for the plain copy of
-    COPY_BYTES. Writes profiles/pmc_traffic.json, keyed by the kernel sources' hash."""
+    COPY_BYTES. Writes out_path (default profiles/pmc_traffic.json), keyed by the kernel
+    sources' hash, and returns the document."""
+    out_path = out_path or PMC_FILE
     def fam(name):
         if "gemm_kernel" in name:
             return "gemm"
@@ -179,7 +181,7 @@ def pmc_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
                            "fetch_scale": f_scale, "write_scale": w_scale},
            "workloads": {workload: res}}
     try:
-        with open(PMC_FILE) as fh:
+        with open(out_path) as fh:
             old = json.load(fh)
         if old.get("kernel_source_hash") == doc["kernel_source_hash"]:
             old["workloads"].update(doc["workloads"])
@@ -187,10 +189,11 @@ def pmc_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
             doc = old
     except (OSError, ValueError):
         pass
-    with open(PMC_FILE, "w") as fh:
+    with open(out_path, "w") as fh:
         json.dump(doc, fh, indent=1, sort_keys=True)
         fh.write("\n")
     print(json.dumps(doc))
+    return doc
 
 
 def cpu_baseline(g, cfg, target_s, act_of=None):
