@@ -4,7 +4,8 @@ The accumulators stay bit-exact; the fp32 pre-activation is the plain epilogue's
 evaluated in binary32 on the GPU and in binary64 by the oracle, so an output may be the adjacent
 fp16/bf16 value only next to a rounding midpoint (tests.gpu_util.act_outputs_match), and such
 elements must stay rare. Every GEMM kernel is covered: four waves per tile, eight waves
-splitting K, 256 x 256 long-K tiles, row-major and tiled codes, int4 codes and the FP6 path.
+splitting K, 256 x 256 long-K tiles, Xq fragments in registers, row-major and tiled codes,
+int4 codes and the FP6 path.
 ("SAM 3.1 Multiplex INT8/INT4 ConvRot" page, "Future improvements": fusion and fewer
 dispatches; the activation itself is not on the pages.)
 """
@@ -43,6 +44,7 @@ def _scales(rng, M, N, K, bits):
 CASES = [(300, 1040, 1024, 8, "tiled"),      # 4 waves per tile, ragged M and N
          (1000, 1040, 1024, 8, "tiled"),     # 36 tiles, 16 steps: 8 waves splitting K
          (4100, 2080, 3072, 8, "tiled"),     # > 256 tiles, K = 3072 bytes: 256 x 256 tiles
+         (4100, 2064, 1536, 8, "tiled"),     # > 256 tiles, K = 1536 bytes: Xq in registers
          (600, 2064, 1024, 8, "rows"),       # row-major codes
          (2000, 6144, 3072, 4, "rows"),      # row-major int4 codes on enough tiles for the
                                              # 128-byte-row kernel without an activation

@@ -230,6 +230,50 @@ def test_gemm_n2_choice_parity(M, N, K, bits, layout):
         assert np.array_equal(bits_from_dev(Y)[rows], ref), io
 
 
+# Shapes with more 256 x 128 tiles than CUs and K of 1024, 1536 or 2048 bytes: with int8 codes
+# in the tiled layout and an fp16/bf16 output the launcher loads Xq fragments straight into
+# registers (one kernel per K, the k loop unrolled); int32 output, row-major or int4 codes take
+# the four-wave LDS kernel. Ragged in M and N; compared on sampled rows (all N columns).
+XR_CASES = [(4100, 2064, 1024, 8), (2600, 3088, 1536, 8), (3000, 2960, 2048, 8),
+            (4100, 2064, 2048, 4)]
+
+
+@pytest.mark.parametrize("M,N,K,bits", XR_CASES)
+@pytest.mark.parametrize("layout", ["rows", "tiled"])
+def test_gemm_xr_choice_parity(M, N, K, bits, layout):
+    need_gpu()
+    print("xr-choice case M=%d N=%d K=%d bits=%d %s" % (M, N, K, bits, layout), flush=True)
+    rng = np.random.default_rng(M + 3 * N + K + bits)
+    A = _random_codes(rng, M, K, bits)
+    B = _random_codes(rng, N, K, bits)
+    packed = oracle.pack_codes(A, bits)
+    if layout == "tiled":
+        Ad = torch.from_numpy(tile_codes(packed, M, K, bits, pad_fill=0x77)).cuda()
+        xl = rq.RQ_X_TILED
+    else:
+        Ad = torch.from_numpy(packed).cuda()
+        xl = rq.RQ_X_ROWS
+    Bd = torch.from_numpy(oracle.pack_codes(B, bits)).cuda()
+    sx = (rng.random(M) * 0.05).astype(np.float32)
+    sw = (rng.random(N) * 2e-4).astype(np.float32)
+    b = rng.normal(0, 0.01, N).astype(np.float32)
+    dev = lambda a: torch.from_numpy(a).cuda()
+    acc = rq.gemm_s32(Ad, Bd, bits=bits, K=K, x_layout=xl, M=M)
+    ys = {io: rq.gemm_dequant(Ad, dev(sx), Bd, dev(sw), dev(b), bits=bits, K=K, x_layout=xl,
+                              out_dtype=torch.float16 if io == "f16" else torch.bfloat16)
+          for io in ("f16", "bf16")}
+    y_nb = rq.gemm_dequant(Ad, dev(sx), Bd, dev(sw), None, bits=bits, K=K, x_layout=xl,
+                           out_dtype=torch.float16)
+    torch.cuda.synchronize()
+    rows = _sample_rows(M, M + N + 1)
+    ref_acc = oracle.gemm_s32(np.ascontiguousarray(A[rows]), B)
+    assert np.array_equal(acc.cpu().numpy()[rows], ref_acc)
+    for io, Y in ys.items():
+        ref = oracle.epilogue(ref_acc, sx[rows], sw, b, IO_CODE[io])
+        assert np.array_equal(bits_from_dev(Y)[rows], ref), io
+    assert np.array_equal(bits_from_dev(y_nb)[rows], oracle.epilogue(ref_acc, sx[rows], sw, None, IO_CODE["f16"]))
+
+
 # Shapes the launcher sends to its 128-byte-row 256 x 256-tile kernel (row-major codes, K of
 # 1536-3071 bytes and at least 192 such tiles), ragged in M and N; compared on sampled rows
 # (all N columns).

@@ -65,19 +65,57 @@ constexpr int kLoadsPerStep = kStageBytes / 1024 / 4;   // wave-wide 1 KB copies
 // hash already separates rows r and r + 8, so the swizzle only spreads rows r..r+7 (bits 1-2).
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 3; }
 
+// Raw buffer resource (stride 0, gfx9 32-bit data-format word) over `bytes` bytes from `base`.
+// The copies below go through MUBUF loads straight to LDS rather than the FLAT-encoded
+// global_load_lds: the compiler counts a FLAT copy as an LDS access too and then waits for
+// every copy in flight before each fragment read, while MUBUF copies leave its LDS-read waits
+// partial (the kernels wait for their copies themselves, before each barrier). Each resource
+// starts at its tile's first row, so the 32-bit offsets stay small for any operand size.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
 // One wave copies 16 rows x 64 B (1 KB) of a K-contiguous operand into LDS rows
-// [row0, row0 + 16) of a tile. Lane l fills LDS position (row0 + l/4, chunk l%4), which holds
-// global chunk (l%4) ^ swz(row). Rows past the end of the operand re-read its last row (their
-// results are never stored).
-__device__ __forceinline__ void copy_rows(const uint8_t* __restrict__ g, int64_t ld, int row0,
-                                          int grow0, int gmax, int k0, uint8_t* lds_tile,
-                                          int lane) {
+// [row0, row0 + 16) of a tile. `rs` starts at the tile's first row (stride ld bytes) and holds
+// `nrows` rows. Lane l fills LDS position (row0 + l/4, chunk l%4), which holds global chunk
+// (l%4) ^ swz(row). Rows past the end of the operand re-read its last row (their results are
+// never stored).
+__device__ __forceinline__ void copy_rows(__amdgpu_buffer_rsrc_t rs, int ld, int row0, int nrows,
+                                          int k0, uint8_t* lds_tile, int lane) {
   const int r = row0 + (lane >> 2);
   const int c = (lane & 3) ^ swz(r);
-  int gr = grow0 + r;
-  gr = gr < gmax ? gr : gmax - 1;
-  const uint8_t* src = g + (int64_t)gr * ld + k0 + 16 * c;
-  __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(lds_tile + row0 * kBKB), 16, 0, 0);
+  const int gr = r < nrows ? r : nrows - 1;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds_tile + row0 * kBKB), 16,
+                                           gr * ld + k0 + 16 * c, 0, 0, 0);
+}
+
+// Tiled Xq ([256-row panel][64-byte k step][256 rows][64 B], rows padded to the panel): the
+// 16 rows [row0, row0 + 16) of k step k0 / 64 are one contiguous 1 KB block. `rs` starts at
+// the panel.
+__device__ __forceinline__ void copy_rows_tiled(__amdgpu_buffer_rsrc_t rs, int row0, int k0,
+                                                uint8_t* lds_tile, int lane) {
+  const int r = row0 + (lane >> 2);
+  const int c = (lane & 3) ^ swz(r);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds_tile + row0 * kBKB), 16,
+                                           (k0 << 8) + (r << 6) + 16 * c, 0, 0, 0);
+}
+
+// The two operands' resources for the tile at rows (m0, n0): Xq from its panel (tiled) or
+// first row, Wq from row n0, rows clamped to the operand.
+struct TileRsrc {
+  __amdgpu_buffer_rsrc_t x, w;
+  int xrows, wrows;
+};
+template <bool XT>
+__device__ __forceinline__ TileRsrc tile_rsrc(const uint8_t* Xq, const uint8_t* Wq, int M, int N,
+                                              int Kb, int m0, int n0, int bn) {
+  TileRsrc t;
+  t.xrows = M - m0 < kBM ? M - m0 : kBM;
+  t.wrows = N - n0 < bn ? N - n0 : bn;
+  t.x = XT ? buffer_rsrc(Xq + (int64_t)m0 * Kb, kBM * Kb)
+           : buffer_rsrc(Xq + (int64_t)m0 * Kb, t.xrows * Kb);
+  t.w = buffer_rsrc(Wq + (int64_t)n0 * Kb, t.wrows * Kb);
+  return t;
 }
 
 __device__ __forceinline__ v4i read_frag(const uint8_t* lds_tile, int row, int chunk) {
@@ -137,6 +175,7 @@ __global__ __launch_bounds__(kThreads * SPLIT, 2 / SPLIT) void gemm_kernel(
   // Stage s of this group holds the Xq tile (256 rows) then the Wq tile (128 rows), 64 B per
   // row, for k step SPLIT*j + grp.
   uint8_t* const ring = lds + grp * kStageBytes;
+  const TileRsrc rs = tile_rsrc<XT>(Xq, Wq, M, N, Kb, m0, n0, kBN);
   auto issue = [&](int stage, int j) {
     const int k0 = (SPLIT * j + grp) * kBKB;
     uint8_t* tX = ring + stage * kSlot;
@@ -144,19 +183,13 @@ __global__ __launch_bounds__(kThreads * SPLIT, 2 / SPLIT) void gemm_kernel(
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       if constexpr (XT) {
-        // Tiled Xq ([256-row panel][64-byte k step][256 rows][64 B], rows padded to the panel):
-        // the 16 rows of this copy are one contiguous 1 KB block.
-        const int row0 = (wave * 4 + i) * 16;
-        const int r = row0 + (lane >> 2);
-        const int c = (lane & 3) ^ swz(r);
-        const uint8_t* src = Xq + (((int64_t)tm * (Kb >> 6) + (k0 >> 6)) << 14) + (r << 6) + 16 * c;
-        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(tX + row0 * kBKB), 16, 0, 0);
+        copy_rows_tiled(rs.x, (wave * 4 + i) * 16, k0, tX, lane);
       } else {
-        copy_rows(Xq, Kb, (wave * 4 + i) * 16, m0, M, k0, tX, lane);
+        copy_rows(rs.x, Kb, (wave * 4 + i) * 16, rs.xrows, k0, tX, lane);
       }
     }
 #pragma unroll
-    for (int i = 0; i < 2; i++) copy_rows(Wq, Kb, (wave * 2 + i) * 16, n0, N, k0, tW, lane);
+    for (int i = 0; i < 2; i++) copy_rows(rs.w, Kb, (wave * 2 + i) * 16, rs.wrows, k0, tW, lane);
   };
 
   // Fragments of one 32-byte k slice: 4 Wq row blocks and this wave's 2 Xq row blocks.
@@ -377,6 +410,7 @@ __global__ __launch_bounds__(512, 1) void gemm_n2_kernel(
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[a][b][r] = 0;
 
+  const TileRsrc rs = tile_rsrc<XT>(Xq, Wq, M, N, Kb, m0, n0, 256);
   auto issue = [&](int stage, int kt) {
     const int k0 = kt * kBKB;
     uint8_t* tX = lds + stage * kStageN2;
@@ -385,16 +419,13 @@ __global__ __launch_bounds__(512, 1) void gemm_n2_kernel(
     for (int i = 0; i < 2; i++) {
       const int row0 = (wave_all * 2 + i) * 16;
       if constexpr (XT) {
-        const int r = row0 + (lane >> 2);
-        const int c = (lane & 3) ^ swz(r);
-        const uint8_t* src = Xq + (((int64_t)tm * (Kb >> 6) + (k0 >> 6)) << 14) + (r << 6) + 16 * c;
-        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(tX + row0 * kBKB), 16, 0, 0);
+        copy_rows_tiled(rs.x, row0, k0, tX, lane);
       } else {
-        copy_rows(Xq, Kb, row0, m0, M, k0, tX, lane);
+        copy_rows(rs.x, Kb, row0, rs.xrows, k0, tX, lane);
       }
     }
 #pragma unroll
-    for (int i = 0; i < 2; i++) copy_rows(Wq, Kb, (wave_all * 2 + i) * 16, n0, N, k0, tW, lane);
+    for (int i = 0; i < 2; i++) copy_rows(rs.w, Kb, (wave_all * 2 + i) * 16, rs.wrows, k0, tW, lane);
   };
 
   const int rsub = lane & 31, fhalf = lane >> 5;
@@ -519,6 +550,172 @@ __global__ __launch_bounds__(512, 1) void gemm_n2_kernel(
   tile_epilogue_act<BITS, OUT, 2>(act, acc, scales, lds + wave_all * (64 * 256), wave * 64, lane, m0, n0 + 128 * grp, M, N, Y);
 }
 
+// Xq fragments straight into registers (int8 codes, tiled Xq, output in fp16/bf16). In the
+// 256 x 128 tile each wave multiplies only its own 64 Xq rows, so staging Xq through LDS buys
+// no reuse: here each wave loads its two 32-row fragments per 32-byte slice with 16-byte global
+// loads (lane l: row l % 32, 16-byte chunk 2 s + l / 32 of the step), two k steps ahead in three
+// register sets, and only Wq (shared by the four waves) goes through a 3-deep LDS ring. Per
+// k step the LDS reads drop from 6 to 4 fragments per slice. NK = Kb / 64 is a compile-time
+// count so that the register sets are named statically (the k loop unrolls fully).
+constexpr int kStageW = kBN * kBKB;                      // 8 KB of Wq per ring stage
+constexpr int kStageOutXr = 4 * 64 * 256;                // epilogue staging: 4 waves x 16 KB
+constexpr int kLdsXr = (kStageOutXr > kStages * kStageW ? kStageOutXr : kStages * kStageW) +
+                       (2 * kBN + kBM) * 4;
+
+template <int OUT, int NK>
+__global__ __launch_bounds__(kThreads, 2) void gemm_xr_kernel(
+    const uint8_t* __restrict__ Xq, const float* __restrict__ sx, const uint8_t* __restrict__ Wq,
+    const float* __restrict__ sw, const float* __restrict__ bias, void* __restrict__ Y, int M,
+    int N, int Kb, int tiles_m, int tiles_n, int act) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsXr];
+  constexpr int kScalesOff = kLdsXr - (2 * kBN + kBM) * 4;
+  constexpr int nk = NK;
+
+  const int ntiles = tiles_m * tiles_n;
+  const int per_xcd = (ntiles + 7) >> 3;
+  const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (logical >= ntiles) return;
+  const int tm = logical / tiles_n;
+  const int tn = logical - tm * tiles_n;
+  const int m0 = tm * kBM, n0 = tn * kBN;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  float my_sw = 0.0f, my_b = 0.0f, my_sx = 0.0f;
+  {
+    const int n = n0 + (int)threadIdx.x, m = m0 + (int)threadIdx.x;
+    if (threadIdx.x < kBN && n < N) {
+      my_sw = sw[n];
+      my_b = bias ? bias[n] : 0.0f;
+    }
+    if (threadIdx.x < kBM && m < M) my_sx = sx[m];
+  }
+
+  v16i acc[4][2];
+#pragma unroll
+  for (int a = 0; a < 4; a++)
+#pragma unroll
+    for (int b = 0; b < 2; b++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[a][b][r] = 0;
+
+  // Tiled Xq: the panel's k step kk is a 256-row x 64-byte block at (tm * nk + kk) * 16 KB.
+  const uint8_t* xbase = Xq + ((int64_t)tm * nk << 14) + (wave * 64 + (lane & 31)) * 64 + (lane >> 5) * 16;
+  auto load_x = [&](int kk, v4i (&xr)[2][2]) __attribute__((always_inline)) {
+    const uint8_t* p = xbase + ((int64_t)kk << 14);
+#pragma unroll
+    for (int b = 0; b < 2; b++)
+#pragma unroll
+      for (int s = 0; s < 2; s++) xr[b][s] = *reinterpret_cast<const v4i*>(p + b * 2048 + s * 32);
+  };
+  const int wrows = N - n0 < kBN ? N - n0 : kBN;
+  const __amdgpu_buffer_rsrc_t wrs = buffer_rsrc(Wq + (int64_t)n0 * Kb, wrows * Kb);
+  auto issue_w = [&](int slot, int kk) __attribute__((always_inline)) {
+    uint8_t* tW = lds + slot * kStageW;
+#pragma unroll
+    for (int i = 0; i < 2; i++) copy_rows(wrs, Kb, (wave * 2 + i) * 16, wrows, kk * kBKB, tW, lane);
+  };
+  const int rsub = lane & 31, fhalf = lane >> 5;
+  auto read_w = [&](int slot, int ks, v4i (&wf)[4]) __attribute__((always_inline)) {
+    const uint8_t* tW = lds + slot * kStageW;
+#pragma unroll
+    for (int a = 0; a < 4; a++) wf[a] = read_frag(tW, a * 32 + rsub, 2 * ks + fhalf);
+  };
+  auto mfma_slice = [&](const v4i (&wf)[4], const v4i (&xr)[2][2], int s) __attribute__((always_inline)) {
+#pragma unroll
+    for (int a = 0; a < 4; a++)
+#pragma unroll
+      for (int b = 0; b < 2; b++)
+        acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[a], xr[b][s], acc[a][b], 0, 0, 0);
+  };
+
+  // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8),
+  // issued through the builtin so that the compiler's own wait insertion accounts for them.
+  constexpr int kWaitLgkm0 = 0xC07F;                                   // lgkmcnt(0)
+  auto vm_wait = [](auto n_tag) __attribute__((always_inline)) {
+    constexpr int n = decltype(n_tag)::value;
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
+  };
+  // Step kt computes with register set kt % 3 and at its start loads step kt + 2 into set
+  // (kt + 2) % 3, which step kt - 1 has finished with; Wq runs two steps ahead through the LDS
+  // ring, slot kt % 3. Loads per step, in issue order: 2 Wq copies, then 4 Xq loads.
+  // Why the ring is race free: the copies issued in step kt fill slot (kt + 2) % 3 =
+  // (kt - 1) % 3, whose last reads (slice 1 of step kt - 1, issued at that step's start) every
+  // wave completed (lgkmcnt(0)) before the barrier of step kt - 1; the reads of slot
+  // (kt + 1) % 3 follow the barrier of step kt, which every wave passes only after its own
+  // copies of step kt + 1 have landed.
+  v4i xs[3][2][2];
+  issue_w(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_x(0, xs[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  issue_w(1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  load_x(1, xs[1]);
+  __builtin_amdgcn_sched_barrier(0);
+  vm_wait(std::integral_constant<int, 10>{});   // Wq of step 0 landed (10 loads issued after it)
+  {
+    float* e_sw = reinterpret_cast<float*>(lds + kScalesOff);
+    if (threadIdx.x < kBN) {
+      e_sw[threadIdx.x] = my_sw;
+      e_sw[kBN + threadIdx.x] = my_b;
+    }
+    if (threadIdx.x < kBM) e_sw[2 * kBN + threadIdx.x] = my_sx;
+  }
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  v4i wf0[4];
+  read_w(0, 0, wf0);
+
+  auto body = [&](auto load_tag, auto mid_tag, int kt, v4i (&xc)[2][2], v4i (&xn)[2][2]) __attribute__((always_inline)) {
+    constexpr bool LOAD = decltype(load_tag)::value;    // kt + 2 < nk
+    constexpr bool MID = decltype(mid_tag)::value;      // kt + 1 < nk
+    v4i wf1[4];
+    read_w(kt % kStages, 1, wf1);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (LOAD) {
+      issue_w((kt + 2) % kStages, kt + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      load_x(kt + 2, xn);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mfma_slice(wf0, xc, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (MID) {
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      // Wq of step kt + 1 landed: issued after it were the 4 Xq loads of step kt + 1 and, when
+      // LOAD, the 6 loads of step kt + 2.
+      if constexpr (LOAD) {
+        vm_wait(std::integral_constant<int, 10>{});
+      } else {
+        vm_wait(std::integral_constant<int, 4>{});
+      }
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      read_w((kt + 1) % kStages, 0, wf0);
+    }
+    mfma_slice(wf1, xc, 1);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // DS read (next slice 0)
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  using T = std::true_type;
+  using F = std::false_type;
+#pragma unroll
+  for (int kt = 0; kt < nk - 2; kt++) body(T{}, T{}, kt, xs[kt % 3], xs[(kt + 2) % 3]);
+  body(F{}, T{}, nk - 2, xs[(nk - 2) % 3], xs[nk % 3]);
+  body(F{}, F{}, nk - 1, xs[(nk - 1) % 3], xs[(nk + 1) % 3]);
+  __syncthreads();
+  const float* scales = reinterpret_cast<const float*>(lds + kScalesOff);
+  tile_epilogue_act<8, OUT, 2>(act, acc, scales, lds + wave * (64 * 256), wave * 64, lane, m0, n0, M, N, Y);
+}
+
 template <int BITS, int OUT, bool XT>
 hipError_t launch(const void* Xq, const float* sx, const void* Wq, const float* sw,
                   const float* bias, int64_t M, int64_t N, int64_t Kb, void* Y, int act, hipStream_t st) {
@@ -530,6 +727,10 @@ hipError_t launch(const void* Xq, const float* sx, const void* Wq, const float* 
   // k steps split between two wave groups), when the steps divide evenly and are long enough
   // (at least 8 per group) for the split to pay for the final exchange; measured 4-8% faster
   // on 168-tile launches with 64 steps, and slower with 1 step per group.
+  // Enough tiles to fill the machine, int8 codes in the tiled layout and K = 1024, 1536 or
+  // 2048 bytes: Xq fragments straight into registers; measured 5-7% faster than four waves
+  // staging both operands through LDS (and 2% slower on int4 codes, whose unpacking keeps the
+  // matrix cores the tighter limit).
   // Enough tiles to fill the machine and long K (at least 48 steps): 256 x 256 tiles halve the
   // operand bytes each CU moves per MFMA; measured 6-12% faster at K = 3072-6144 bytes, and
   // 5% slower at K = 1024 bytes, where the longer prologue and epilogue per tile dominate.
@@ -537,7 +738,18 @@ hipError_t launch(const void* Xq, const float* sx, const void* Wq, const float* 
     hipLaunchKernelGGL((gemm_kernel<BITS, OUT, XT, 2>), dim3(grid), dim3(2 * kThreads), 0, st,
                        static_cast<const uint8_t*>(Xq), sx, static_cast<const uint8_t*>(Wq), sw,
                        bias, Y, (int)M, (int)N, (int)Kb, tiles_m, tiles_n, act);
-  } else if (ntiles > kNumCUs && Kb >= 3072) {
+    return hipGetLastError();
+  }
+  if constexpr (BITS == 8 && XT && OUT != kOutS32) {
+    if (ntiles > kNumCUs && (Kb == 1024 || Kb == 1536 || Kb == 2048)) {
+      auto k = Kb == 1024 ? gemm_xr_kernel<OUT, 16> : Kb == 1536 ? gemm_xr_kernel<OUT, 24> : gemm_xr_kernel<OUT, 32>;
+      hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), 0, st, static_cast<const uint8_t*>(Xq), sx,
+                         static_cast<const uint8_t*>(Wq), sw, bias, Y, (int)M, (int)N, (int)Kb,
+                         tiles_m, tiles_n, act);
+      return hipGetLastError();
+    }
+  }
+  if (ntiles > kNumCUs && Kb >= 3072) {
     const int tiles_n2 = (int)((N + 255) / 256);
     const int ntiles2 = tiles_m * tiles_n2;
     hipLaunchKernelGGL((gemm_n2_kernel<BITS, OUT, XT>), dim3(((ntiles2 + 7) / 8) * 8), dim3(512), 0,
