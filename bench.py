@@ -95,6 +95,32 @@ def _read_counter_csv(path):
     return out
 
 
+def _is_gemm(kernel_name):
+    """The library's GEMM kernels: gemm_kernel, gemm_xr_kernel, gemm_n2_kernel, gemm_wide_kernel
+    and gemm_fp6_kernel (template arguments follow the name)."""
+    import re
+    return re.search(r"(?:^|::|\s)gemm_\w*kernel\s*[<(]", kernel_name) is not None
+
+
+def gemm_kernel_name(M, N, K, bits, x_layout, w_layout=0, act=0, s32=False):
+    """The GEMM kernel the launcher picks for a call, by the dispatch rule of gemm_i8.hip,
+    gemm_i8_wide.hip and gemm_fp6.hip (a label for the roofline record)."""
+    from w4a4_integer_quantized_amd import binding as rq
+    if w_layout == rq.RQ_W_FP6:
+        return "gemm_fp6_kernel"
+    Kb = K if bits == 8 else K // 2
+    tiles = -(-M // 256) * -(-N // 128)
+    if x_layout == rq.RQ_X_ROWS and act == 0 and 1536 <= Kb < 3072 and -(-M // 256) * -(-N // 256) >= 192:
+        return "gemm_wide_kernel"
+    if tiles <= 256 and (Kb // 64) % 2 == 0 and Kb // 64 >= 16:
+        return "gemm_kernel (8 waves, split K)"
+    if bits == 8 and x_layout == rq.RQ_X_TILED and not s32 and tiles > 256 and Kb in (1024, 1536, 2048):
+        return "gemm_xr_kernel"
+    if tiles > 256 and Kb >= 3072:
+        return "gemm_n2_kernel"
+    return "gemm_kernel"
+
+
 def mfma_summary(counter_csv, trace_csv, n_simd=1024, n_xcc=8):
     """Reduce a rocprofv3 run with --pmc MfmaUtil SQ_VALU_MFMA_BUSY_CYCLES
     SQ_INSTS_VALU_MFMA_MOPS_I8 GRBM_GUI_ACTIVE --kernel-trace to per-launch figures of the GEMM's
@@ -108,7 +134,7 @@ def mfma_summary(counter_csv, trace_csv, n_simd=1024, n_xcc=8):
             dur[int(r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
     rows = {}
     for did, (name, grid, vals) in _read_counter_csv(counter_csv).items():
-        if "gemm_kernel" in name and did in dur:
+        if _is_gemm(name) and did in dur:
             rows.setdefault(grid, []).append((name, vals, dur[did]))
     grid = max(rows)
     name = rows[grid][0][0]
@@ -147,7 +173,7 @@ def pmc_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, 
     sources' hash, and returns the document."""
     out_path = out_path or PMC_FILE
     def fam(name):
-        if "gemm_kernel" in name:
+        if _is_gemm(name):
             return "gemm"
         if "rotate_quant" in name:
             return "rotate_quant"
@@ -551,7 +577,8 @@ def main():
     dc = calls[dom.name]
     tr = traffic_from_counters(cfg.workload, "gemm")
     traffic = tr["bytes"] if tr else None
-    kname = "gemm_fp6_kernel" if wl == rq.RQ_W_FP6 else "gemm_kernel"
+    kname = gemm_kernel_name(M, dom.N, dom.K, bits, rq.RQ_X_FP6 if wl == rq.RQ_W_FP6 else rq.RQ_X_TILED, wl,
+                             act_of[dom.name])
     roofline = {"bound": "mfma", "kernel": "%s (%s: %dx%dx%d, W%dA%d)" % (kname, dom.name, M, dom.N, dom.K, bits, bits),
                 "achieved": dc["gemm_TOPS"], "peak": peak_gemm, "unit": "TOP/s",
                 "frac": dc["gemm_mfma_frac"], "traffic": traffic,

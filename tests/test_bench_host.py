@@ -94,3 +94,30 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stdout
+
+
+def test_gemm_kernel_names_are_recognised():
+    for name in (GEMM, "void convrot::(anonymous namespace)::gemm_xr_kernel<1, 16>(unsigned char const*)",
+                 "void convrot::(anonymous namespace)::gemm_n2_kernel<8, 2, true>(unsigned char const*)",
+                 "convrot::(anonymous namespace)::gemm_wide_kernel<4, 1>(unsigned char const*)",
+                 "void convrot::(anonymous namespace)::gemm_fp6_kernel<1, 1>(unsigned char const*)"):
+        assert bench._is_gemm(name), name
+    for name in (RQ, COPY, "void convrot::(anonymous namespace)::weight_quant_mse_kernel(float const*)"):
+        assert not bench._is_gemm(name), name
+
+
+def test_gemm_kernel_label_follows_the_launch_rule():
+    from w4a4_integer_quantized_amd import binding as rq
+    T, R = rq.RQ_X_TILED, rq.RQ_X_ROWS
+    # The shapes the GPU parity tests send to each kernel.
+    assert bench.gemm_kernel_name(41472, 3072, 1024, 8, T) == "gemm_xr_kernel"
+    assert bench.gemm_kernel_name(4100, 2064, 1024, 8, T) == "gemm_xr_kernel"
+    assert bench.gemm_kernel_name(4100, 2064, 1024, 8, T, s32=True) == "gemm_kernel"
+    assert bench.gemm_kernel_name(4100, 2064, 2048, 4, T) == "gemm_kernel"        # int4: Kb = 1024
+    assert bench.gemm_kernel_name(4100, 2064, 1024, 8, R) == "gemm_kernel"
+    assert bench.gemm_kernel_name(1000, 1040, 1024, 8, T).startswith("gemm_kernel (8 waves")
+    assert bench.gemm_kernel_name(4100, 2080, 3072, 8, T) == "gemm_n2_kernel"
+    assert bench.gemm_kernel_name(8192, 1536, 6144, 8, T) == "gemm_n2_kernel"
+    assert bench.gemm_kernel_name(2048, 6144, 1536, 8, R) == "gemm_wide_kernel"
+    assert bench.gemm_kernel_name(2048, 6144, 1536, 8, R, act=1) == "gemm_kernel"
+    assert bench.gemm_kernel_name(257, 512, 4096, 4, rq.RQ_X_FP6, rq.RQ_W_FP6) == "gemm_fp6_kernel"
