@@ -274,6 +274,28 @@ def test_gemm_xr_choice_parity(M, N, K, bits, layout):
     assert np.array_equal(bits_from_dev(y_nb)[rows], oracle.epilogue(ref_acc, sx[rows], sw, None, IO_CODE["f16"]))
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 32784, 1024), (300, 16400, 2048), (64, 32784, 1536)])
+def test_gemm_xr_few_rows_many_tiles(M, N, K):
+    """Xq fragments in registers with one or two token panels spread over more tiles than CUs:
+    the panel's pad rows are loaded and multiplied but never stored. Every element compared."""
+    need_gpu()
+    print("xr-few-rows case M=%d N=%d K=%d" % (M, N, K), flush=True)
+    rng = np.random.default_rng(M + N + K)
+    A = _random_codes(rng, M, K, 8)
+    B = _random_codes(rng, N, K, 8)
+    Ad = torch.from_numpy(tile_codes(oracle.pack_codes(A, 8), M, K, 8, pad_fill=0x81)).cuda()
+    Bd = torch.from_numpy(oracle.pack_codes(B, 8)).cuda()
+    sx = (rng.random(M) * 0.05).astype(np.float32)
+    sw = (rng.random(N) * 2e-4).astype(np.float32)
+    b = rng.normal(0, 0.01, N).astype(np.float32)
+    dev = lambda a: torch.from_numpy(a).cuda()
+    Y = rq.gemm_dequant(Ad, dev(sx), Bd, dev(sw), dev(b), bits=8, K=K, x_layout=rq.RQ_X_TILED,
+                        out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = oracle.epilogue(oracle.gemm_s32(A, B), sx, sw, b, IO_CODE["bf16"])
+    assert np.array_equal(bits_from_dev(Y), ref)
+
+
 # Shapes the launcher sends to its 128-byte-row 256 x 256-tile kernel (row-major codes, K of
 # 1536-3071 bytes and at least 192 such tiles), ragged in M and N; compared on sampled rows
 # (all N columns).
