@@ -14,7 +14,8 @@
 //     while one is in its epilogue, prologue or at a barrier, the other keeps the matrix cores
 //     busy.
 //   * K is staged 64 bytes per step (64 int8 or 128 int4 codes) through a 3-deep LDS ring
-//     filled by direct global->LDS 16-byte loads (prefetch distance 2 steps). Rows are 64 B;
+//     filled by direct global->LDS 16-byte loads (MUBUF buffer loads to LDS, see buffer_rsrc;
+//     prefetch distance 2 steps). Rows are 64 B;
 //     the 16-byte chunk c of row r sits at c ^ swz(r), which keeps the MFMA fragment reads
 //     (ds_read_b128, 32 rows x 2 chunks per wave) free of bank conflicts on gfx950's LDS
 //     (see swz). The fragment reads of the next slice are issued between the MFMAs of the
@@ -33,6 +34,10 @@
 //     tile instead (one 512-thread workgroup per CU, 146 KB LDS): two groups of four take the
 //     even and the odd k steps in lockstep, each with its own half of a doubled ring, then swap
 //     halves of their accumulators through LDS so that each wave finishes one 32-row block.
+//   * Launches with more tiles than CUs, int8 codes in the tiled layout, an fp16/bf16 output
+//     and K of 1024, 1536 or 2048 bytes load each wave's Xq fragments straight into registers
+//     instead (gemm_xr_kernel): a wave multiplies only its own 64 Xq rows, so only Wq, which
+//     the four waves share, goes through LDS.
 //   * Launches with more tiles than CUs and at least 48 k steps use 256 x 256 tiles instead:
 //     eight waves in two groups of four share one 256-row Xq stage and each takes its own
 //     128-row half of a 256-row Wq stage (one 512-thread workgroup per CU, 132 KB LDS), which
