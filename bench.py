@@ -114,7 +114,7 @@ def gemm_kernel_name(M, N, K, bits, x_layout, w_layout=0, act=0, s32=False):
         return "gemm_wide_kernel"
     if tiles <= 256 and (Kb // 64) % 2 == 0 and Kb // 64 >= 16:
         return "gemm_kernel (8 waves, split K)"
-    if bits == 8 and x_layout == rq.RQ_X_TILED and not s32 and tiles > 256 and Kb in (1024, 1536, 2048):
+    if bits == 8 and x_layout == rq.RQ_X_TILED and tiles > 256 and Kb in (1024, 1536, 2048):
         return "gemm_xr_kernel"
     if tiles > 256 and Kb >= 3072:
         return "gemm_n2_kernel"
@@ -384,6 +384,205 @@ def synth_workload_name(key):
     return synth.CONFIGS[key].workload
 
 
+GELU_ACT = {"gelu_erf": 1, "gelu_tanh": 2}     # rq.RQ_ACT_GELU_ERF / RQ_ACT_GELU_TANH
+
+
+class WorkloadRun:
+    """One workload on the GPU: its weights quantized offline, a ring of input / output buffer
+    sets larger than the Infinity Cache, and the hot path's calls with every argument marshalled
+    once, before any timing. A step is rq_rotq_linear for each linear of the workload, in
+    order, on one dedicated stream."""
+
+    def __init__(self, key, stream, w4_fp6=False, unfused_gelu=False, min_sets=3):
+        import numpy as np
+        import torch
+        import w4a4_integer_quantized_amd as rq
+        from w4a4_integer_quantized_amd import synth
+        self.rq, self.torch, self.np = rq, torch, np
+        self.key = key
+        self.cfg = cfg = synth.CONFIGS[key]
+        log("generating %s" % cfg.workload)
+        self.g = g = synth.generate(key)
+        self.tdt = tdt = torch.float16 if cfg.io == "f16" else torch.bfloat16
+        self.dev = dev = torch.device("cuda:0")
+        self.stream, self.sptr = stream, stream.cuda_stream
+        self.bits, self.M = bits, M = cfg.bits, cfg.M
+        self.unfused_gelu = unfused_gelu
+        # 4-bit codes run on the int8 matrix cores by default; --w4-fp6 runs them on the FP6 ones
+        # (weights and activations stored as FP6 tiles; identical results).
+        self.wl = wl = rq.RQ_W_FP6 if bits == 4 and w4_fp6 else rq.RQ_W_ROWS
+        self.xl = rq.RQ_X_FP6 if wl == rq.RQ_W_FP6 else rq.RQ_X_TILED
+        # Offline weight quantization (timed once, reported separately).
+        self.Wq, self.Ws, self.B = {}, {}, {}
+        self.wq_ms = 0.0
+        for lin in cfg.linears:
+            Wd = torch.from_numpy(g["W"][lin.name]).to(dev)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            self.Wq[lin.name], self.Ws[lin.name] = rq.quantize_weights(Wd, bits=bits, w_layout=wl)
+            torch.cuda.synchronize()
+            self.wq_ms += (time.perf_counter() - t0) * 1e3
+            self.B[lin.name] = torch.from_numpy(g["bias"][lin.name]).to(dev)
+            del Wd
+        # MLP pairs: the GELU between the linears runs in the first linear's epilogue (or, with
+        # unfused_gelu, as a torch op on the GPU between the two calls, inside the step).
+        self.act_of = {lin.name: rq.RQ_ACT_NONE for lin in cfg.linears}
+        if not unfused_gelu:
+            for lin in cfg.linears:
+                if lin.source in GELU_ACT:
+                    self.act_of[lin.producer] = GELU_ACT[lin.source]
+        self.cfgc = {lin.name: rq.make_cfg(bits, w_layout=wl, act=self.act_of[lin.name]) for lin in cfg.linears}
+        self.cfg_split = {lin.name: rq.make_cfg(bits, x_layout=self.xl, w_layout=wl, act=self.act_of[lin.name])
+                          for lin in cfg.linears}
+        self.xdt = rq.RQ_F16 if cfg.io == "f16" else rq.RQ_BF16
+        # Ring of buffer sets (X copies, outputs, workspace) larger than the Infinity Cache.
+        x_host = torch.from_numpy(g["x_bits"].view(np.int16)).view(tdt)
+        ws_bytes = {lin.name: rq.workspace_size(M, lin.K, bits, w_layout=wl) for lin in cfg.linears}
+        set_bytes = x_host.numel() * 2 + sum(M * lin.N * 2 + ws_bytes[lin.name] for lin in cfg.linears)
+        self.R = R = max(min_sets, min(8, math.ceil(3 * MALL_BYTES / set_bytes)))
+        self.set_bytes = set_bytes
+        self.sets = []
+        for _ in range(R):
+            st = {"X": x_host.to(dev), "Y": {}, "ws": {}}
+            for lin in cfg.linears:
+                st["Y"][lin.name] = torch.empty((M, lin.N), dtype=tdt, device=dev)
+                st["ws"][lin.name] = torch.empty((ws_bytes[lin.name],), dtype=torch.uint8, device=dev)
+            self.sets.append(st)
+        log("%s: ring of %d buffer sets, %.0f MB each" % (key, R, set_bytes / 1e6))
+        self._marshal(ws_bytes)
+
+    def _input(self, st, lin):
+        if lin.source == "x":
+            return st["X"]
+        if self.act_of[lin.producer] != self.rq.RQ_ACT_NONE:
+            return st["Y"][lin.producer]            # the producer's epilogue applied the GELU
+        return None                                 # computed by a torch op inside the step
+
+    def _marshal(self, ws_bytes):
+        """Every buffer's shape is checked here, once; the timed loop then passes the stored
+        integer pointers and ctypes configs straight to the C entry points."""
+        import ctypes
+        rq, torch, M = self.rq, self.torch, self.M
+        lib = rq.load()
+        self.fn_linear, self.fn_rq, self.fn_gemm = lib.rq_rotq_linear, lib.rq_rotate_quantize, lib.rq_gemm_dequant
+        self.calls = []          # per set: [(lin, gelu_src or None, args of rq_rotq_linear)]
+        self.split = []          # per set: [(lin, gelu_src, args of rq_rotate_quantize, args of rq_gemm_dequant)]
+        for st in self.sets:
+            calls, split = [], []
+            for lin in self.cfg.linears:
+                X = self._input(st, lin)
+                gelu_src = None
+                if X is None:
+                    # The torch op writes into a buffer of its own, allocated once per set.
+                    X = torch.empty((M, lin.K), dtype=self.tdt, device=self.dev)
+                    st.setdefault("G", {})[lin.name] = X
+                    gelu_src = (st["Y"][lin.producer], X, "tanh" if lin.source == "gelu_tanh" else "none")
+                assert X.shape == (M, lin.K) and X.dtype == self.tdt and X.is_contiguous(), (lin.name, X.shape)
+                Y, ws = st["Y"][lin.name], st["ws"][lin.name]
+                assert Y.shape == (M, lin.N) and Y.dtype == self.tdt and Y.is_contiguous(), lin.name
+                assert ws.numel() >= ws_bytes[lin.name], lin.name
+                wq, wsc, b = self.Wq[lin.name], self.Ws[lin.name], self.B[lin.name]
+                assert wq.numel() * wq.element_size() == rq.rq_weight_bytes(lin.N, lin.K, self.cfgc[lin.name]), lin.name
+                assert wsc.shape == (lin.N,) and b.shape == (lin.N,) and wsc.dtype == b.dtype == torch.float32
+                cfg_ref = ctypes.byref(self.cfgc[lin.name])
+                calls.append((lin, gelu_src, (X.data_ptr(), self.xdt, M, lin.K, wq.data_ptr(), wsc.data_ptr(),
+                                              lin.N, b.data_ptr(), cfg_ref, Y.data_ptr(), ws.data_ptr(),
+                                              ws.numel(), self.sptr)))
+                # The split calls use the fused call's own workspace layout: [codes | x_scale].
+                cs = self.cfg_split[lin.name]
+                xq = ws.data_ptr()
+                xs = xq + (rq.rq_codes_bytes(M, lin.K, cs) + 255) // 256 * 256
+                cs_ref = ctypes.byref(cs)
+                split.append((lin, gelu_src,
+                              (X.data_ptr(), self.xdt, M, lin.K, cs_ref, xq, xs, self.sptr),
+                              (xq, xs, wq.data_ptr(), wsc.data_ptr(), b.data_ptr(), M, lin.N, lin.K, cs_ref,
+                               Y.data_ptr(), self.xdt, self.sptr)))
+            self.calls.append(calls)
+            self.split.append(split)
+
+    def _gelu(self, src):
+        Yp, out, approx = src
+        self.torch.ops.aten.gelu.out(Yp, approximate=approx, out=out)
+
+    def step(self, i):
+        fn = self.fn_linear
+        for lin, gelu_src, a in self.calls[i % self.R]:
+            if gelu_src is not None:
+                self._gelu(gelu_src)
+            st = fn(*a)
+            if st:
+                raise self.rq.ConvRotError(st, "rq_rotq_linear", self.rq.load().rq_last_error_detail().decode())
+
+    def split_step(self, i, evs):
+        """The same two kernels per call through the split entry points, with HIP events
+        recorded on the launch stream between them."""
+        for c, (lin, gelu_src, a_rq, a_gm) in enumerate(self.split[i % self.R]):
+            if gelu_src is not None:
+                self._gelu(gelu_src)
+            evs[3 * c].record(self.stream)
+            st = self.fn_rq(*a_rq)
+            evs[3 * c + 1].record(self.stream)
+            st |= self.fn_gemm(*a_gm)
+            evs[3 * c + 2].record(self.stream)
+            if st:
+                raise self.rq.ConvRotError(st, "split step", self.rq.load().rq_last_error_detail().decode())
+
+    def ops_per_step(self):
+        return sum(2 * self.M * lin.N * lin.K for lin in self.cfg.linears)
+
+    def time(self, steps, warmup, peak_gemm):
+        """Timed steps (wall clock between device synchronizations) and per-kernel event times."""
+        torch, np, M, bits = self.torch, self.np, self.M, self.bits
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms_per_step = wall * 1e3 / steps
+        tops = self.ops_per_step() * steps / wall / 1e12
+        log("%s: timed %d steps: %.4f ms/step, %.1f TOPS" % (self.key, steps, ms_per_step, tops))
+        nl = len(self.cfg.linears)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3 * nl)] for _ in range(steps)]
+        for i in range(min(warmup, 3)):
+            self.split_step(i, ev[0])
+        torch.cuda.synchronize()
+        for i in range(steps):
+            self.split_step(i, ev[i])
+        torch.cuda.synchronize()
+        calls = {}
+        kern_us = 0.0
+        for c, lin in enumerate(self.cfg.linears):
+            rq_t = np.array([ev[i][3 * c].elapsed_time(ev[i][3 * c + 1]) for i in range(steps)])
+            gm_t = np.array([ev[i][3 * c + 1].elapsed_time(ev[i][3 * c + 2]) for i in range(steps)])
+            rq_ms, gm_ms = float(rq_t.mean()), float(gm_t.mean())
+            kern_us += (rq_ms + gm_ms) * 1e3
+            ops = 2 * M * lin.N * lin.K
+            rq_bytes = M * lin.K * 2 + M * lin.K * bits // 8 + 4 * M
+            gemm_bytes = M * lin.K * bits // 8 + lin.N * lin.K * bits // 8 + 8 * lin.N + 4 * M + M * lin.N * 2
+            calls[lin.name] = {
+                "M": M, "N": lin.N, "K": lin.K,
+                "gemm_kernel": gemm_kernel_name(M, lin.N, lin.K, bits, self.xl, self.wl, self.act_of[lin.name]),
+                "act": self.act_of[lin.name],
+                "rotate_quant_us": round(rq_ms * 1e3, 2),
+                "rotate_quant_GBps": round(rq_bytes / (rq_ms * 1e-3) / 1e9, 1),
+                "rotate_quant_hbm_frac": round(rq_bytes / (rq_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                "gemm_us": round(gm_ms * 1e3, 2),
+                "gemm_TOPS": round(ops / (gm_ms * 1e-3) / 1e12, 1),
+                "gemm_mfma_frac": round(ops / (gm_ms * 1e-3) / 1e12 / peak_gemm, 4),
+                "call_us": round((rq_ms + gm_ms) * 1e3, 2),
+                "call_TOPS": round(ops / ((rq_ms + gm_ms) * 1e-3) / 1e12, 1),
+                "call_int8_peak_frac": round(ops / ((rq_ms + gm_ms) * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+                "rotate_quant_alg_bytes": rq_bytes, "gemm_alg_bytes": gemm_bytes, "gemm_alg_ops": ops,
+                "rotate_quant_us_p10_p50_p90": [round(float(np.percentile(rq_t, p)) * 1e3, 2) for p in (10, 50, 90)],
+                "gemm_us_p10_p50_p90": [round(float(np.percentile(gm_t, p)) * 1e3, 2) for p in (10, 50, 90)],
+            }
+        return {"ms_per_step": ms_per_step, "tops": tops, "calls": calls,
+                "kernel_us_per_step": round(kern_us, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -391,6 +590,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="vit_attn")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="time only the headline workload (the default also runs every other one)")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the context measurements (vendor library GEMM, weight-quantizer rules)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration)")
@@ -424,162 +627,24 @@ def main():
     from w4a4_integer_quantized_amd import synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    cfg = synth.CONFIGS[args.workload]
-    log("generating %s" % cfg.workload)
-    g = synth.generate(args.workload)
-    tdt = torch.float16 if cfg.io == "f16" else torch.bfloat16
     dev = torch.device("cuda:0")
     # All work goes to one dedicated stream (default priority). Dependent kernels on the legacy
     # null stream measured ~10% slower per step here (extra synchronization between launches).
     stream = torch.cuda.Stream(device=dev)
     torch.cuda.set_stream(stream)
-    bits, M = cfg.bits, cfg.M
 
-    # 4-bit codes run on the int8 matrix cores by default; --w4-fp6 runs them on the FP6 ones
-    # (weights and activations stored as FP6 tiles; identical results). On the W4A4 workload the
-    # FP6 GEMM is faster but its activation quantizer slower, and the step measured slower.
-    wl = rq.RQ_W_FP6 if bits == 4 and args.w4_fp6 else rq.RQ_W_ROWS
-    # Offline weight quantization (timed once, reported separately).
-    Wq, Ws, B = {}, {}, {}
-    wq_ms = 0.0
-    for lin in cfg.linears:
-        Wd = torch.from_numpy(g["W"][lin.name]).to(dev)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        Wq[lin.name], Ws[lin.name] = rq.quantize_weights(Wd, bits=bits, w_layout=wl)
-        torch.cuda.synchronize()
-        wq_ms += (time.perf_counter() - t0) * 1e3
-        B[lin.name] = torch.from_numpy(g["bias"][lin.name]).to(dev)
-        del Wd
+    run = WorkloadRun(args.workload, stream, w4_fp6=args.w4_fp6, unfused_gelu=args.unfused_gelu)
+    cfg, g, M, bits = run.cfg, run.g, run.M, run.bits
+    peak_gemm = PEAK_FP6_TOPS if run.wl == rq.RQ_W_FP6 else PEAK_INT8_TOPS
+    res = run.time(args.steps, args.warmup, peak_gemm)
+    calls, tops, ms_per_step = res["calls"], res["tops"], res["ms_per_step"]
 
-    # Ring of buffer sets (X copies, outputs, workspace) larger than the Infinity Cache.
-    x_host = torch.from_numpy(g["x_bits"].view(np.int16)).view(tdt)
-    set_bytes = x_host.numel() * 2
-    for lin in cfg.linears:
-        set_bytes += M * lin.N * 2 + rq.workspace_size(M, lin.K, bits, w_layout=wl)
-    R = max(3, min(8, math.ceil(3 * MALL_BYTES / set_bytes)))
-    sets = []
-    for _ in range(R):
-        s = {"X": x_host.to(dev), "Y": {}, "ws": {}}
-        for lin in cfg.linears:
-            s["Y"][lin.name] = torch.empty((M, lin.N), dtype=tdt, device=dev)
-            s["ws"][lin.name] = torch.empty((rq.workspace_size(M, lin.K, bits, w_layout=wl),), dtype=torch.uint8, device=dev)
-        sets.append(s)
-    log("ring of %d buffer sets, %.0f MB each" % (R, set_bytes / 1e6))
-    # MLP pairs: the GELU between the linears runs in the first linear's epilogue (or, with
-    # --unfused-gelu, as a torch op on the GPU between the two calls).
-    gelu_act = {"gelu_erf": rq.RQ_ACT_GELU_ERF, "gelu_tanh": rq.RQ_ACT_GELU_TANH}
-    act_of = {lin.name: rq.RQ_ACT_NONE for lin in cfg.linears}
-    if not args.unfused_gelu:
-        for lin in cfg.linears:
-            if lin.source in gelu_act:
-                act_of[lin.producer] = gelu_act[lin.source]
-    cfgc = {lin.name: rq.make_cfg(bits, w_layout=wl, act=act_of[lin.name]) for lin in cfg.linears}
-    peak_gemm = PEAK_FP6_TOPS if wl == rq.RQ_W_FP6 else PEAK_INT8_TOPS
-    cfg_tiled = {lin.name: rq.make_cfg(bits, x_layout=rq.RQ_X_FP6 if wl == rq.RQ_W_FP6 else rq.RQ_X_TILED,
-                                       w_layout=wl, act=act_of[lin.name]) for lin in cfg.linears}
-    xdt = rq.RQ_F16 if cfg.io == "f16" else rq.RQ_BF16
-    sptr = stream.cuda_stream
-
-    def lin_input(s, lin):
-        if lin.source == "x":
-            X = s["X"]
-        elif act_of[lin.producer] != rq.RQ_ACT_NONE:
-            X = s["Y"][lin.producer]          # the producer's epilogue applied the GELU
-        else:
-            approx = "tanh" if lin.source == "gelu_tanh" else "none"
-            X = torch.nn.functional.gelu(s["Y"][lin.producer], approximate=approx)
-        # The raw entry points take bare pointers: check every buffer's shape on the host first.
-        assert X.shape == (M, lin.K) and X.dtype == tdt and X.is_contiguous(), (lin.name, X.shape)
-        assert s["Y"][lin.name].shape == (M, lin.N), lin.name
-        assert s["ws"][lin.name].numel() >= rq.workspace_size(M, lin.K, bits, w_layout=wl), lin.name
-        assert Wq[lin.name].numel() * Wq[lin.name].element_size() == \
-            rq.rq_weight_bytes(lin.N, lin.K, cfgc[lin.name]), lin.name
-        return X
-
-    def step(i):
-        s = sets[i % R]
-        for lin in cfg.linears:
-            X = lin_input(s, lin)
-            ws = s["ws"][lin.name]
-            st = rq.rq_rotq_linear(X.data_ptr(), xdt, M, lin.K, Wq[lin.name].data_ptr(),
-                                   Ws[lin.name].data_ptr(), lin.N, B[lin.name].data_ptr(), cfgc[lin.name],
-                                   s["Y"][lin.name].data_ptr(), ws.data_ptr(), ws.numel(), sptr)
-            if st != rq.RQ_OK:
-                raise rq.ConvRotError(st, "rq_rotq_linear", rq.load().rq_last_error_detail().decode())
-
-    ops_per_step = sum(2 * M * lin.N * lin.K for lin in cfg.linears)
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    log("warmup done (%d steps)" % args.warmup)
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    tops = ops_per_step * args.steps / wall / 1e12
-    log("timed %d steps: %.3f ms/step, %.1f TOPS" % (args.steps, ms_per_step, tops))
-
-    # Per-kernel durations: the same two kernels per call (rotate+quantize, GEMM+epilogue)
-    # launched through the split entry points with the fused call's tiled code layout, with
-    # HIP events between them on the stream.
-    nl = len(cfg.linears)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3 * nl)] for _ in range(args.steps)]
-
-    def split_step(i, evs):
-        s = sets[i % R]
-        for c, lin in enumerate(cfg.linears):
-            X = lin_input(s, lin)
-            # The fused call's own layout: workspace = [tiled Xq | x_scale].
-            xq = s["ws"][lin.name].data_ptr()
-            ct = cfg_tiled[lin.name]
-            xs = xq + (rq.rq_codes_bytes(M, lin.K, ct) + 255) // 256 * 256
-            evs[3 * c].record(stream)
-            st = rq.rq_rotate_quantize(X.data_ptr(), xdt, M, lin.K, ct, xq, xs, sptr)
-            evs[3 * c + 1].record(stream)
-            st |= rq.rq_gemm_dequant(xq, xs, Wq[lin.name].data_ptr(), Ws[lin.name].data_ptr(),
-                                     B[lin.name].data_ptr(), M, lin.N, lin.K, ct,
-                                     s["Y"][lin.name].data_ptr(), xdt, sptr)
-            evs[3 * c + 2].record(stream)
-            assert st == rq.RQ_OK
-
-    for i in range(min(args.warmup, 3)):
-        split_step(i, ev[0])
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        split_step(i, ev[i])
-    torch.cuda.synchronize()
-    calls = {}
-    for c, lin in enumerate(cfg.linears):
-        rq_t = np.array([ev[i][3 * c].elapsed_time(ev[i][3 * c + 1]) for i in range(args.steps)])
-        gm_t = np.array([ev[i][3 * c + 1].elapsed_time(ev[i][3 * c + 2]) for i in range(args.steps)])
-        rq_ms, gm_ms = float(rq_t.mean()), float(gm_t.mean())
-        ops = 2 * M * lin.N * lin.K
-        rq_bytes = M * lin.K * 2 + M * lin.K * bits // 8 + 4 * M
-        gemm_bytes = M * lin.K * bits // 8 + lin.N * lin.K * bits // 8 + 8 * lin.N + 4 * M + M * lin.N * 2
-        calls[lin.name] = {
-            "M": M, "N": lin.N, "K": lin.K,
-            "rotate_quant_us": round(rq_ms * 1e3, 2),
-            "rotate_quant_GBps": round(rq_bytes / (rq_ms * 1e-3) / 1e9, 1),
-            "rotate_quant_hbm_frac": round(rq_bytes / (rq_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            "gemm_us": round(gm_ms * 1e3, 2),
-            "gemm_TOPS": round(ops / (gm_ms * 1e-3) / 1e12, 1),
-            "gemm_mfma_frac": round(ops / (gm_ms * 1e-3) / 1e12 / peak_gemm, 4),
-            "call_TOPS": round(ops / ((rq_ms + gm_ms) * 1e-3) / 1e12, 1),
-            "call_int8_peak_frac": round(ops / ((rq_ms + gm_ms) * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
-            "rotate_quant_alg_bytes": rq_bytes, "gemm_alg_bytes": gemm_bytes, "gemm_alg_ops": ops,
-            "rotate_quant_us_p10_p50_p90": [round(float(np.percentile(rq_t, p)) * 1e3, 2) for p in (10, 50, 90)],
-            "gemm_us_p10_p50_p90": [round(float(np.percentile(gm_t, p)) * 1e3, 2) for p in (10, 50, 90)],
-        }
     dom = max(cfg.linears, key=lambda l: l.N * l.K)
     dc = calls[dom.name]
     tr = traffic_from_counters(cfg.workload, "gemm")
     traffic = tr["bytes"] if tr else None
-    kname = gemm_kernel_name(M, dom.N, dom.K, bits, rq.RQ_X_FP6 if wl == rq.RQ_W_FP6 else rq.RQ_X_TILED, wl,
-                             act_of[dom.name])
-    roofline = {"bound": "mfma", "kernel": "%s (%s: %dx%dx%d, W%dA%d)" % (kname, dom.name, M, dom.N, dom.K, bits, bits),
+    roofline = {"bound": "mfma", "kernel": "%s (%s: %dx%dx%d, W%dA%d)" % (dc["gemm_kernel"], dom.name, M, dom.N, dom.K,
+                                                                           bits, bits),
                 "achieved": dc["gemm_TOPS"], "peak": peak_gemm, "unit": "TOP/s",
                 "frac": dc["gemm_mfma_frac"], "traffic": traffic,
                 "avg_launch_us": dc["gemm_us"], "alg_ops_per_launch": dc["gemm_alg_ops"],
@@ -597,40 +662,61 @@ def main():
     qerr = {}
     rs = np.random.default_rng(12345).choice(M, min(M, 512), replace=False)
     for lin in cfg.linears:
-        xs_bits = g["x_bits"] if lin.source == "x" else None
-        if xs_bits is None:
+        if lin.source != "x":
             continue          # second-layer inputs come from the GPU's own GELU; skip
-        xr = torch.from_numpy(xs_bits[rs].view(np.int16)).view(tdt).float().numpy().astype(np.float64)
+        xr = torch.from_numpy(g["x_bits"][rs].view(np.int16)).view(run.tdt).float().numpy().astype(np.float64)
         ref = xr @ g["W"][lin.name].astype(np.float64).T + g["bias"][lin.name].astype(np.float64)
-        if act_of[lin.name] != rq.RQ_ACT_NONE:
-            ref = synth.gelu(ref, "gelu_erf" if act_of[lin.name] == rq.RQ_ACT_GELU_ERF else "gelu_tanh")
-        got = sets[0]["Y"][lin.name][torch.from_numpy(rs).to(dev)].float().cpu().numpy().astype(np.float64)
+        if run.act_of[lin.name] != rq.RQ_ACT_NONE:
+            ref = synth.gelu(ref, "gelu_erf" if run.act_of[lin.name] == rq.RQ_ACT_GELU_ERF else "gelu_tanh")
+        got = run.sets[0]["Y"][lin.name][torch.from_numpy(rs).to(dev)].float().cpu().numpy().astype(np.float64)
         qerr[lin.name] = round(float(np.linalg.norm(got - ref) / np.linalg.norm(ref)), 6)
 
+    gelu_cfg = {}
+    if any(l.source in GELU_ACT for l in cfg.linears):
+        gelu_cfg = {"gelu": "torch op between the linears" if args.unfused_gelu else
+                    "fused into the first linear's epilogue"}
     out = {
         "metric": "rotq_linear TOPS (rotate+quant+GEMM) and % of MI355X INT8 MFMA peak",
         "value": round(tops, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "int4 codes as fp6 e2m3" if wl == rq.RQ_W_FP6 else "int8",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "int4 codes as fp6 e2m3" if run.wl == rq.RQ_W_FP6 else "int8",
         "data": "synthetic",
         "config": {"workload": cfg.workload, "M": M, "K": cfg.K, "N": [l.N for l in cfg.linears],
-                   "io": cfg.io, "bits": bits, "calls_per_step": nl,
-                   **({"gelu": "torch op between the linears" if args.unfused_gelu else
-                       "fused into the first linear's epilogue"}
-                      if any(l.source in gelu_act for l in cfg.linears) else {})},
+                   "io": cfg.io, "bits": bits, "calls_per_step": len(cfg.linears), **gelu_cfg},
         "int8_peak_frac": round(tops / PEAK_INT8_TOPS, 4),
+        "kernel_us_per_step": res["kernel_us_per_step"],
         "roofline": roofline, "roofline_rotate_quant": roofline_rq, "calls": calls,
-        "weight_quant_ms_offline": round(wq_ms, 3), "buffer_sets": R,
+        "weight_quant_ms_offline": round(run.wq_ms, 3), "buffer_sets": run.R,
         "quant_error_rel_frobenius_vs_fp64": qerr,
     }
     out["gpu_state_after_timing"] = gpu_state()
-    log("library int8 GEMM on the %s shape (context)" % dom.name)
-    out["context_library_int8_gemm"] = library_int8_gemm(torch, M, dom.N, dom.K)
-    log("offline weight quantizer rules on %s" % dom.name)
-    out["weight_quantizer"] = offline_weight_quant(rq, torch, g["W"][dom.name], bits, dev)
+
+    # Every other workload, each timed the same way (fewer steps; not part of `value`).
+    if not args.no_other_workloads:
+        others = {}
+        for key in synth.CONFIGS:
+            if key == args.workload:
+                continue
+            other = WorkloadRun(key, stream, w4_fp6=args.w4_fp6, unfused_gelu=args.unfused_gelu)
+            pg = PEAK_FP6_TOPS if other.wl == rq.RQ_W_FP6 else PEAK_INT8_TOPS
+            r = other.time(max(20, args.steps // 2), max(5, args.warmup // 2), pg)
+            others[key] = {"workload": other.cfg.workload, "ms_per_step": round(r["ms_per_step"], 4),
+                           "step_TOPS": round(r["tops"], 1),
+                           "step_int8_peak_frac": round(r["tops"] / PEAK_INT8_TOPS, 4),
+                           "kernel_us_per_step": r["kernel_us_per_step"], "calls": r["calls"]}
+            del other
+            torch.cuda.empty_cache()
+        out["workloads"] = others
+
+    if not args.no_context:
+        log("library int8 GEMM on the %s shape (context)" % dom.name)
+        out["context_library_int8_gemm"] = library_int8_gemm(torch, M, dom.N, dom.K)
+        log("offline weight quantizer rules on %s" % dom.name)
+        out["weight_quantizer"] = offline_weight_quant(rq, torch, g["W"][dom.name], bits, dev)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle, ~%.0f s)" % args.cpu_seconds)
-        out["cpu_baseline"] = cpu_baseline(g, cfg, args.cpu_seconds, act_of)
+        out["cpu_baseline"] = cpu_baseline(g, cfg, args.cpu_seconds, run.act_of)
     print(json.dumps(out))
 
 

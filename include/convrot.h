@@ -13,9 +13,11 @@
  *   rotation   per 128-wide block of K: unnormalized Walsh-Hadamard transform in fp32 with the
  *              butterfly stages h = 1, 2, 4, ..., 64 in this order (Sylvester order, no signs);
  *              the 1/sqrt(128) normalization is folded into the scale.
- *   scale      a = max |u| over the whole row; a == 0 -> scale 0, codes 0;
- *              else inv = fl(q_max / a), scale = fl(fl(a * fl(1/sqrt 128)) / q_max),
- *              code = round_half_even(fl(u * inv)); q_max = 127 (8-bit) or 7 (4-bit).
+ *   scale      a = max |u| over the whole row, inv = fl(q_max / a); q_max = 127 (8-bit) or
+ *              7 (4-bit). a == 0, or a so small that inv is +inf (a below about
+ *              q_max * 2^-128, reachable from bf16 / f32 inputs only) -> scale 0 and codes 0:
+ *              the row is quantized as a zero row. Else scale = fl(fl(a * fl(1/sqrt 128)) /
+ *              q_max), code = round_half_even(fl(u * inv)).
  *   storage    8-bit: int8 [rows, K]; 4-bit: uint8 [rows, K/2], two's-complement nibbles,
  *              low nibble = even k.
  *   activation code layouts (rq_qconfig.x_layout):
@@ -91,7 +93,8 @@ enum { RQ_W_ROWS = 0, RQ_W_FP6 = 1 };                   /* weight code layouts (
 /* Weight-scale rules of rq_quantize_weights. Each picks a clipping threshold t per row and
  * then quantizes exactly as above with a replaced by t: inv = fl(q_max / t),
  * scale = fl(fl(t * fl(1/sqrt 128)) / q_max), code = clamp(round_half_even(fl(u * inv)),
- * -q_max, q_max); t = 0 gives scale 0 and codes 0.
+ * -q_max, q_max); t = 0, or a t whose inv is +inf, gives scale 0 and codes 0 (the zero-row
+ * rule above; in RQ_W_MSE such a candidate is the all-zero quantization of the row).
  *   RQ_W_ABSMAX   t = a = max |u| of the row (the default; the rule of the activations).
  *   RQ_W_MSE      MSE-optimized clipping ("Quantization recipe", step 3: the converter picks
  *                 the clipping scale with the least squared error). t = fl(a * alpha_i),
@@ -193,8 +196,10 @@ rq_status rq_gemm_dequant(const void *Xq, const float *x_scale, const void *Wq,
                           int64_t K, const rq_qconfig *cfg, void *Y, int32_t y_dtype,
                           void *stream);
 
-/* Same mainloop, storing the exact int32 accumulators acc[M, N] = sum_k Xq[m,k] * Wq[n,k]
- * (for bit-exact checks); Xq in cfg->x_layout. */
+/* The exact int32 accumulators acc[M, N] = sum_k Xq[m,k] * Wq[n,k] (for bit-exact checks);
+ * Xq in cfg->x_layout. For every shape, bits and layout this runs the kernel, launch geometry
+ * and mainloop that rq_gemm_dequant runs with cfg->act == RQ_ACT_NONE (and so rq_rotq_linear,
+ * whose codes are in RQ_X_TILED or RQ_X_FP6), with the int32 store in place of the epilogue. */
 rq_status rq_gemm_s32(const void *Xq, const void *Wq, int64_t M, int64_t N, int64_t K,
                       const rq_qconfig *cfg, int32_t *acc, void *stream);
 

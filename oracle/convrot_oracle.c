@@ -151,10 +151,11 @@ static float load_elem(const void *x, int dtype, int64_t idx) {
 /*
  * For each row r of x [rows, K] (dtype f32 / f16 / bf16 raw bits):
  *   u   = f32(x[r, :]);  if rotate: u <- FWHT_128 of each 128-block (unnormalized)
- *   a   = max_k |u_k|
- *   a == 0:  scale = 0, codes = 0
- *   else:    inv = fl(q_max / a);  scale = fl(fl(a * c) / q_max)  (c = fl(1/sqrt 128), or 1
- *            without rotation);  p_k = fl(u_k * inv);  q_k = round-half-even(p_k)
+ *   a   = max_k |u_k|;  inv = fl(q_max / a)
+ *   a == 0, or inv = +inf (a too small for its reciprocal to be finite, below about
+ *            q_max * 2^-128):  scale = 0, codes = 0 (the row is quantized as a zero row)
+ *   else:    scale = fl(fl(a * c) / q_max)  (c = fl(1/sqrt 128), or 1 without rotation);
+ *            p_k = fl(u_k * inv);  q_k = round-half-even(p_k)
  * codes: int8 [rows, K] (unpacked, in [-q_max, q_max]); scales: f32 [rows];
  * pre (optional, may be NULL): f32 [rows, K], the pre-rounding values p_k.
  * Returns 0, or -1 if a code fell outside [-q_max, q_max] (cannot happen; checked anyway),
@@ -174,14 +175,14 @@ int orc_quantize_rows(const void *x, int dtype, int64_t rows, int64_t K, int bit
       for (int64_t b = 0; b < K / ORC_BLOCK; b++) orc_fwht128(u + b * ORC_BLOCK);
     float a = 0.0f;
     for (int64_t k = 0; k < K; k++) a = fmaxf(a, fabsf(u[k]));
-    if (a == 0.0f) {
+    const float inv = (a > 0.0f) ? qmax / a : 0.0f;
+    if (a == 0.0f || isinf(inv)) {
       scales[r] = 0.0f;
       for (int64_t k = 0; k < K; k++) {
         codes[r * K + k] = 0;
         if (pre) pre[r * K + k] = 0.0f;
       }
     } else {
-      float inv = qmax / a;
       float ac = a * c;
       scales[r] = ac / qmax;
       for (int64_t k = 0; k < K; k++) {
@@ -207,13 +208,17 @@ int orc_quantize_rows(const void *x, int dtype, int64_t rows, int64_t K, int bit
 float orc_clip_alpha(int i) { return (float)(100 - i) / 100.0f; }
 
 /* Quantize the rotated row u[K] against clipping threshold t (> 0): inv = fl(q_max / t),
- * s = fl(fl(t * c) / q_max), q_k = clamp(rne(fl(u_k * inv)), -q_max, q_max). Returns s and, in
- * err, sum_k (u_k * c - s * q_k)^2 evaluated in binary64 in increasing k (the products are
- * exact in binary64; the differences, squares and sums are rounded). */
+ * s = fl(fl(t * c) / q_max), q_k = clamp(rne(fl(u_k * inv)), -q_max, q_max); a threshold whose
+ * reciprocal overflows (inv = +inf) quantizes the row to zero (s = 0, codes 0), the rule of
+ * orc_quantize_rows. Returns s and, in err, sum_k (u_k * c - s * q_k)^2 evaluated in binary64 in
+ * increasing k (the products are exact in binary64; the differences, squares and sums are
+ * rounded). */
 static float quantize_clipped(const float *u, int64_t K, float t, float qmax, float c, int8_t *q,
                               double *err) {
-  const float inv = qmax / t;
-  const float s = (t * c) / qmax;
+  const float inv0 = qmax / t;
+  const int zero = isinf(inv0);
+  const float inv = zero ? 0.0f : inv0;
+  const float s = zero ? 0.0f : (t * c) / qmax;
   double e = 0.0;
   for (int64_t k = 0; k < K; k++) {
     float v = nearbyintf(u[k] * inv);
@@ -277,8 +282,9 @@ int orc_quantize_rows_mse(const void *x, int dtype, int64_t rows, int64_t K, int
 
 /* Tensor-wise scale (the HSWQ model card's int8_tensorwise variant, here after the same
  * rotation): one absmax A over the whole rotated tensor; every row is quantized with
- * inv = fl(q_max / A) and gets the same scale fl(fl(A * c) / q_max). A zero tensor gets scales
- * 0 and codes 0. pre (or NULL) receives fl(u * inv). Rotation always on. */
+ * inv = fl(q_max / A) and gets the same scale fl(fl(A * c) / q_max). A zero tensor, or one whose
+ * A is too small for a finite inv, gets scales 0 and codes 0. pre (or NULL) receives
+ * fl(u * inv). Rotation always on. */
 int orc_quantize_tensorwise(const void *x, int dtype, int64_t rows, int64_t K, int bits,
                             int8_t *codes, float *scales, float *pre) {
   if (K <= 0 || K % ORC_BLOCK != 0 || (bits != 8 && bits != 4) || rows < 0) return -2;
@@ -293,10 +299,11 @@ int orc_quantize_tensorwise(const void *x, int dtype, int64_t rows, int64_t K, i
     for (int64_t b = 0; b < K / ORC_BLOCK; b++) orc_fwht128(ur + b * ORC_BLOCK);
     for (int64_t k = 0; k < K; k++) A = fmaxf(A, fabsf(ur[k]));
   }
-  const float inv = (A > 0.0f) ? qmax / A : 0.0f;
-  const float s = (A * c) / qmax;
+  float inv = (A > 0.0f) ? qmax / A : 0.0f;
+  if (isinf(inv)) inv = 0.0f;            /* reciprocal overflow: the zero-row rule */
+  const float s = (inv != 0.0f) ? (A * c) / qmax : 0.0f;
   for (int64_t r = 0; r < rows; r++) {
-    scales[r] = (A > 0.0f) ? s : 0.0f;
+    scales[r] = s;
     for (int64_t k = 0; k < K; k++) {
       const float p = u[r * K + k] * inv;
       codes[r * K + k] = (int8_t)nearbyintf(p);

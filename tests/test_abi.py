@@ -204,3 +204,74 @@ def test_fp6_test_helpers_follow_e2m3():
         t = fp6_tile(c, P)
         assert t.size == (300 + P - 1) // P * P * 6 * 48
         assert np.array_equal(fp6_untile(t, 300, 384, P), c)
+
+
+# ---- the tensor wrappers' own checks (the C ABI sees only pointers, so shapes, dtypes and
+# buffer sizes are checked in Python before any device access; CPU tensors suffice here) ----
+def _torch_cpu_args(M=64, K=256, N=32, bits=8):
+    import torch
+    X = torch.zeros((M, K), dtype=torch.float16)
+    Wq = torch.zeros((N, K if bits == 8 else K // 2), dtype=torch.int8 if bits == 8 else torch.uint8)
+    return X, Wq, torch.zeros(N), torch.zeros(N)
+
+
+@pytest.mark.parametrize("bad", ["w_scale_f16", "w_scale_len", "bias_f16", "bias_len", "wq_other_k",
+                                 "wq_other_bits", "out_shape", "out_dtype", "x_f32", "x_3d", "ws_small"])
+def test_rotq_linear_wrapper_rejects_bad_buffers(bad):
+    import torch
+    X, Wq, ws, b = _torch_cpu_args()
+    kw = {}
+    if bad == "w_scale_f16":
+        ws = ws.half()
+    elif bad == "w_scale_len":
+        ws = torch.zeros(48)
+    elif bad == "bias_f16":
+        b = b.half()
+    elif bad == "bias_len":
+        b = torch.zeros(16)
+    elif bad == "wq_other_k":
+        Wq = torch.zeros((32, 512), dtype=torch.int8)
+    elif bad == "wq_other_bits":
+        kw["bits"] = 4                         # int8 [N, K] is twice the bytes of 4-bit codes
+    elif bad == "out_shape":
+        kw["out"] = torch.empty((64, 16), dtype=torch.float16)
+    elif bad == "out_dtype":
+        kw["out"] = torch.empty((64, 32), dtype=torch.bfloat16)
+    elif bad == "x_f32":
+        X = X.float()
+    elif bad == "x_3d":
+        X = X.view(4, 16, 256)
+    elif bad == "ws_small":
+        kw["workspace"] = torch.empty((100,), dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        rq.rotq_linear(X, Wq, ws, b, **kw)
+
+
+def test_gemm_wrappers_reject_bad_buffers():
+    import torch
+    Wq = torch.zeros((32, 256), dtype=torch.int8)
+    Xq = torch.zeros((64, 256), dtype=torch.int8)
+    xs, ws = torch.zeros(64), torch.zeros(32)
+    with pytest.raises(ValueError):            # Xq shorter than M rows of codes
+        rq.gemm_dequant(Xq[:10], xs, Wq, ws)
+    with pytest.raises(ValueError):            # x_scale of the wrong dtype
+        rq.gemm_dequant(Xq, xs.double(), Wq, ws)
+    with pytest.raises(ValueError):            # w_scale shorter than Wq's rows
+        rq.gemm_dequant(Xq, xs, Wq, ws[:16])
+    with pytest.raises(ValueError):            # 4-bit codes need half the bytes
+        rq.gemm_s32(Xq, Wq, bits=4)
+    with pytest.raises(ValueError):            # tiled codes of M rows need the padded size
+        rq.gemm_s32(torch.zeros(64 * 256, dtype=torch.uint8), Wq, x_layout=rq.RQ_X_TILED, M=64)
+    with pytest.raises(ValueError):            # tiled layout without M
+        rq.gemm_s32(Xq, Wq, x_layout=rq.RQ_X_TILED)
+
+
+def test_wrappers_accept_valid_cpu_buffers_up_to_the_device_check():
+    """Valid shapes pass every size check and stop only at the device check."""
+    import torch
+    X, Wq, ws, b = _torch_cpu_args()
+    with pytest.raises(ValueError, match="device tensor"):
+        rq.rotq_linear(X, Wq, ws, b, workspace=torch.empty(rq.workspace_size(64, 256), dtype=torch.uint8))
+    Xt = torch.zeros(256 * 256, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="device tensor"):
+        rq.gemm_s32(Xt, Wq, x_layout=rq.RQ_X_TILED, M=64)

@@ -112,7 +112,7 @@ def test_gemm_kernel_label_follows_the_launch_rule():
     # The shapes the GPU parity tests send to each kernel.
     assert bench.gemm_kernel_name(41472, 3072, 1024, 8, T) == "gemm_xr_kernel"
     assert bench.gemm_kernel_name(4100, 2064, 1024, 8, T) == "gemm_xr_kernel"
-    assert bench.gemm_kernel_name(4100, 2064, 1024, 8, T, s32=True) == "gemm_kernel"
+    assert bench.gemm_kernel_name(4100, 2064, 1024, 8, T, s32=True) == "gemm_xr_kernel"   # same kernel for int32
     assert bench.gemm_kernel_name(4100, 2064, 2048, 4, T) == "gemm_kernel"        # int4: Kb = 1024
     assert bench.gemm_kernel_name(4100, 2064, 1024, 8, R) == "gemm_kernel"
     assert bench.gemm_kernel_name(1000, 1040, 1024, 8, T).startswith("gemm_kernel (8 waves")

@@ -194,3 +194,36 @@ def test_rounding_step_order_golden():
         assert codes[r, 0] == 127
         assert float(pre[r, 9]) == c["p"]
         assert int(codes[r, 9]) == c["code"] != c["other"]
+
+
+def _inv_overflow_edge(qmax):
+    """Largest binary32 a for which q_max / a rounds to +inf (RNE overflows at or above
+    2^128 - 2^103), and the next binary32 above it, from exact rationals."""
+    limit = Fraction(qmax) / (Fraction(2) ** 128 - Fraction(2) ** 103)
+    a = np.float32(float(limit))
+    while Fraction(float(a)) > limit:
+        a = np.nextafter(a, np.float32(0))
+    while Fraction(float(np.nextafter(a, np.float32(np.inf)))) <= limit:
+        a = np.nextafter(a, np.float32(np.inf))
+    return a, np.nextafter(a, np.float32(np.inf))
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_reciprocal_overflow_rows_are_zero_rows(bits):
+    """A row whose absmax a is too small for fl(q_max / a) to be finite is quantized as a zero
+    row (scale 0, codes 0); one binary32 step above, the ordinary rule applies. A one-hot f32
+    row x = a e_0 rotates to |u_k| = a over its first block (H's first column is all ones)."""
+    qmax = 127 if bits == 8 else 7
+    a_lo, a_hi = _inv_overflow_edge(qmax)
+    assert np.isinf(np.float32(qmax) / a_lo) and np.isfinite(np.float32(qmax) / a_hi)
+    x = np.zeros((4, 256), np.float32)
+    x[0, 0], x[1, 0], x[2, 0], x[3, 0] = a_lo, -a_lo, a_hi, np.float32(2.0 ** -126)
+    codes, s, pre = oracle.quantize_rows(x, oracle.F32, bits, want_pre=True)
+    for r in (0, 1, 3):
+        assert s[r] == 0 and not codes[r].any() and not pre[r].any()
+    # Every |u_k| of the first block equals a: each code is q_max (p = fl(a fl(q_max / a)) is
+    # within two ulps of q_max), the second block stays zero, and the scale is the usual one.
+    assert np.all(codes[2, :128] == qmax) and not codes[2, 128:].any()
+    c32 = np.float32(np.sqrt(2.0) / 16.0)
+    s_exp = np.float32(np.float32(a_hi) * c32) / np.float32(qmax)
+    assert s[2] == s_exp and s[2] > 0

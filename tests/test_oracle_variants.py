@@ -217,3 +217,41 @@ def test_tensorwise_exact(bits):
 def test_tensorwise_zero_tensor():
     c, s, _ = oracle.quantize_tensorwise(np.zeros((3, 128), np.float32), oracle.F32, 8)
     assert not c.any() and not s.any()
+
+
+def test_mse_clip_candidates_with_overflowing_reciprocal_are_zero_rows():
+    """Near the reciprocal-overflow edge some clipping candidates t_i = fl(a alpha_i) have an
+    infinite fl(q_max / t_i): each quantizes the row to zero, so its error is the row's own
+    energy sum_k (u_k c)^2 (binary64, increasing k), and the choice still follows the errors.
+    A row whose a itself overflows is a zero row (scale 0, codes 0)."""
+    from tests.test_oracle_quant import _inv_overflow_edge
+    qmax = 127
+    a_lo, _ = _inv_overflow_edge(qmax)
+    a = np.float32(a_lo * np.float32(1.5))            # alpha = 1 finite; alpha <= 2/3 overflow
+    x = np.zeros((2, 128), np.float32)
+    x[0, 0] = a
+    x[1, 0] = a_lo
+    codes, scales, idx, err = oracle.quantize_rows_mse(x, oracle.F32, 8)
+    c = float(C32)
+    energy = 0.0
+    for k in range(128):
+        d = float(a) * c - 0.0
+        energy += d * d
+    zero_cands = [i for i in range(51) if np.isinf(np.float32(qmax) / np.float32(a * oracle.clip_alpha(i)))]
+    assert zero_cands and zero_cands[0] > 0
+    for i in zero_cands:
+        assert err[0, i] == energy
+    assert idx[0] == 0 and np.all(codes[0] == qmax)   # constant |u|: alpha = 1 has no error
+    assert scales[1] == 0 and not codes[1].any()
+
+
+def test_tensorwise_reciprocal_overflow_is_zero_tensor():
+    from tests.test_oracle_quant import _inv_overflow_edge
+    a_lo, a_hi = _inv_overflow_edge(7)
+    x = np.zeros((3, 128), np.float32)
+    x[1, 0] = a_lo
+    c, s, _ = oracle.quantize_tensorwise(x, oracle.F32, 4)
+    assert not c.any() and not s.any()
+    x[2, 0] = a_hi
+    c, s, _ = oracle.quantize_tensorwise(x, oracle.F32, 4)
+    assert np.all(s == s[0]) and s[0] > 0 and np.all(c[2] == 7)

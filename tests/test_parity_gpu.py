@@ -184,7 +184,7 @@ def test_gemm_split_choice_parity(M, N, K, bits, layout):
     acc = rq.gemm_s32(Ad, Bd, bits=bits, K=K, x_layout=xl, M=M)
     Y = rq.gemm_dequant(Ad, dev(sx), Bd, dev(sw), dev(b), bits=bits, K=K, x_layout=xl)
     torch.cuda.synchronize()
-    rows = _sample_rows(M, M + N) if M * N * K > 2e9 else np.arange(M)
+    rows = np.arange(M)
     ref_acc = oracle.gemm_s32(np.ascontiguousarray(A[rows]), B)
     assert np.array_equal(acc.cpu().numpy()[rows], ref_acc)
     assert np.array_equal(bits_from_dev(Y)[rows], oracle.epilogue(ref_acc, sx[rows], sw, b, oracle.F16))
@@ -222,7 +222,7 @@ def test_gemm_n2_choice_parity(M, N, K, bits, layout):
                               out_dtype=torch.float16 if io == "f16" else torch.bfloat16)
           for io in ("f16", "bf16")}
     torch.cuda.synchronize()
-    rows = _sample_rows(M, M + N)
+    rows = np.arange(M)
     ref_acc = oracle.gemm_s32(np.ascontiguousarray(A[rows]), B)
     assert np.array_equal(acc.cpu().numpy()[rows], ref_acc)
     for io, Y in ys.items():
@@ -232,8 +232,8 @@ def test_gemm_n2_choice_parity(M, N, K, bits, layout):
 
 # Shapes with more 256 x 128 tiles than CUs and K of 1024, 1536 or 2048 bytes: with int8 codes
 # in the tiled layout and an fp16/bf16 output the launcher loads Xq fragments straight into
-# registers (one kernel per K, the k loop unrolled); int32 output, row-major or int4 codes take
-# the four-wave LDS kernel. Ragged in M and N; compared on sampled rows (all N columns).
+# registers (one kernel per K, the k loop unrolled), for the int32 output too; row-major or
+# int4 codes take the four-wave LDS kernel. Ragged in M and N; every element compared.
 XR_CASES = [(4100, 2064, 1024, 8), (2600, 3088, 1536, 8), (3000, 2960, 2048, 8),
             (4100, 2064, 2048, 4)]
 
@@ -265,7 +265,7 @@ def test_gemm_xr_choice_parity(M, N, K, bits, layout):
     y_nb = rq.gemm_dequant(Ad, dev(sx), Bd, dev(sw), None, bits=bits, K=K, x_layout=xl,
                            out_dtype=torch.float16)
     torch.cuda.synchronize()
-    rows = _sample_rows(M, M + N + 1)
+    rows = np.arange(M)
     ref_acc = oracle.gemm_s32(np.ascontiguousarray(A[rows]), B)
     assert np.array_equal(acc.cpu().numpy()[rows], ref_acc)
     for io, Y in ys.items():
@@ -297,15 +297,8 @@ def test_gemm_xr_few_rows_many_tiles(M, N, K):
 
 
 # Shapes the launcher sends to its 128-byte-row 256 x 256-tile kernel (row-major codes, K of
-# 1536-3071 bytes and at least 192 such tiles), ragged in M and N; compared on sampled rows
-# (all N columns).
+# 1536-3071 bytes and at least 192 such tiles), ragged in M and N; every element compared.
 WIDE_CASES = [(2048, 6144, 1536, 8), (1900, 6160, 1536, 8), (2000, 6144, 3072, 4)]
-
-
-def _sample_rows(M, seed):
-    rng = np.random.default_rng(seed)
-    rows = set(range(40)) | set(range(M - 40, M)) | set(int(r) for r in rng.choice(M, 48, replace=False))
-    return np.array(sorted(rows), dtype=np.int64)
 
 
 @pytest.mark.parametrize("M,N,K,bits", WIDE_CASES)
@@ -315,7 +308,7 @@ def test_gemm_wide_tiles_parity(M, N, K, bits):
     rng = np.random.default_rng(M + N + K + bits)
     A = _random_codes(rng, M, K, bits)
     B = _random_codes(rng, N, K, bits)
-    rows = _sample_rows(M, M + 1)
+    rows = np.arange(M)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     Ad, Bd = dev(oracle.pack_codes(A, bits)), dev(oracle.pack_codes(B, bits))
     acc = rq.gemm_s32(Ad, Bd, bits=bits, K=K)
@@ -413,3 +406,59 @@ def test_runtime_errors_are_raised():
     with pytest.raises(rq.ConvRotError) as e:
         rq.rotq_linear(X, Wq, ws, workspace=small)
     assert e.value.status == rq.RQ_EWORKSPACE
+
+
+def _edge_rows(K, io, bits):
+    """Rows at the reciprocal-overflow edge of the zero-row rule: one-hot rows of magnitude a
+    just at and just above the largest a whose fl(q_max / a) is +inf, their negatives, the
+    smallest normal, a tiny but quantizable row and an ordinary one. bf16 rows round the edge
+    values to bf16 (the first at or below it, the first above)."""
+    from tests.test_oracle_quant import _inv_overflow_edge
+    qmax = 127 if bits == 8 else 7
+    a_lo, a_hi = _inv_overflow_edge(qmax)
+    if io == "bf16":
+        lo_b = oracle.bf16_bits_to_f32(oracle.f32_to_bf16_bits(np.array([a_lo], np.float32)))[0]
+        while lo_b > a_lo:
+            lo_b = np.float32(np.uint32(lo_b.view(np.uint32) - (1 << 16)).view(np.float32))
+        a_lo, a_hi = lo_b, np.float32(np.uint32(lo_b.view(np.uint32) + (1 << 16)).view(np.float32))
+    rng = np.random.default_rng(K + bits)
+    x = np.zeros((8, K), np.float32)
+    x[0, 0], x[1, 5], x[2, 0], x[3, K - 1] = a_lo, -a_lo, a_hi, -a_hi
+    x[4, 7] = np.float32(2.0 ** -126)
+    x[5] = rng.normal(0, 1, K).astype(np.float32) * np.float32(1e-30)
+    x[6] = rng.normal(0, 1, K).astype(np.float32)
+    x[7, :130] = a_lo                      # rotates to a block absmax above the edge
+    return x if io == "f32" else synth.to_io_bits(x, io)
+
+
+@pytest.mark.parametrize("K", [256, 1024, 2176])
+@pytest.mark.parametrize("io,bits", [("f32", 8), ("f32", 4), ("bf16", 8), ("bf16", 4)])
+def test_reciprocal_overflow_rows(K, io, bits):
+    """The zero-row rule (a row whose fl(q_max / a) is +inf gets scale 0 and codes 0) on the
+    activation quantizer, fast and generic kernels, and on the weight quantizer's three rules."""
+    need_gpu()
+    xb = _edge_rows(K, io, bits)
+    Xd = dev_from_bits(xb, io)
+    ref_c, ref_s, ref_p = oracle.quantize_rows(xb, IO_CODE[io], bits, want_pre=True)
+    assert ref_s[0] == 0 and ref_s[2] > 0
+    Xq, xs = rq.rotate_quantize(Xd, bits=bits)
+    torch.cuda.synchronize()
+    assert compare_codes(codes_np(Xq), ref_c, ref_p, bits, K) == 0
+    assert np.array_equal(xs.cpu().numpy().view(np.uint32), ref_s.view(np.uint32))
+    for mode in (rq.RQ_W_ABSMAX, rq.RQ_W_MSE):
+        Wq, ws = rq.quantize_weights(Xd, bits=bits, w_scale_mode=mode)
+        torch.cuda.synchronize()
+        if mode == rq.RQ_W_MSE:
+            c, s, _, _ = oracle.quantize_rows_mse(xb, IO_CODE[io], bits)
+        else:
+            c, s = ref_c, ref_s
+        assert np.array_equal(codes_np(Wq).view(np.uint8), oracle.pack_codes(c, bits).view(np.uint8)), mode
+        assert np.array_equal(ws.cpu().numpy().view(np.uint32), s.view(np.uint32)), mode
+    # Tensor-wise: a tensor of edge rows only (its absmax below, then above, the edge).
+    for rows in ([0, 1], [0, 1, 2]):
+        sub = np.ascontiguousarray(xb[rows])
+        Wq, ws = rq.quantize_weights(dev_from_bits(sub, io), bits=bits, w_scale_mode=rq.RQ_W_TENSOR)
+        torch.cuda.synchronize()
+        c, s, _ = oracle.quantize_tensorwise(sub, IO_CODE[io], bits)
+        assert np.array_equal(codes_np(Wq).view(np.uint8), oracle.pack_codes(c, bits).view(np.uint8)), rows
+        assert np.array_equal(ws.cpu().numpy().view(np.uint32), s.view(np.uint32)), rows

@@ -180,6 +180,44 @@ def _dev(t, name):
     return t.data_ptr()
 
 
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _check_2d(t, name, dtypes):
+    """t is a contiguous 2-D tensor of one of `dtypes` (checked before any device access)."""
+    if t.dim() != 2:
+        raise ValueError("%s must be 2-D, got shape %s" % (name, tuple(t.shape)))
+    if t.dtype not in dtypes:
+        raise ValueError("%s dtype %s (expected one of %s)" % (name, t.dtype, ", ".join(map(str, dtypes))))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _check_vec(t, name, n):
+    """t is a contiguous float32 vector of n elements (the C ABI reads exactly n floats)."""
+    torch = _torch()
+    if t.dtype != torch.float32 or t.dim() != 1 or t.shape[0] != n or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous float32 vector of %d elements, got %s %s"
+                         % (name, n, t.dtype, tuple(t.shape)))
+
+
+def _check_bytes(t, name, need, exact):
+    """The C ABI sizes its buffer descriptors from the shapes, not from the allocation: the
+    buffer must hold exactly (or, for outputs and scratch, at least) `need` bytes."""
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    nb = _nbytes(t)
+    if nb < need or (exact and need > 0 and nb != need):
+        raise ValueError("%s holds %d bytes, %s %d" % (name, nb, "expected" if exact else "needs at least", need))
+
+
+def _same_device(*ts):
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise ValueError("tensors are on different devices: %s" % sorted(map(str, devs)))
+
+
 def code_shape(rows: int, K: int, bits: int) -> Tuple[int, int]:
     return (rows, K if bits == 8 else K // 2)
 
@@ -195,6 +233,7 @@ def quantize_weights(W, bits: int = 8, rot: int = 128, stream=None, w_scale_mode
     (RQ_W_FP6, bits 4). w_scale_mode: RQ_W_ABSMAX (per-row absmax), RQ_W_MSE (per-row
     MSE-optimized clipping) or RQ_W_TENSOR (one tensor-wise scale)."""
     torch = _torch()
+    _check_2d(W, "W", (torch.float32, torch.float16, torch.bfloat16))
     N, K = W.shape
     cfg = make_cfg(bits, rot, w_scale_mode=w_scale_mode, w_layout=w_layout)
     if w_layout == RQ_W_ROWS:
@@ -212,6 +251,7 @@ def rotate_quantize(X, bits: int = 8, rot: int = 128, stream=None, x_layout: int
     (RQ_X_ROWS) or a flat uint8 buffer of rq_codes_bytes() in the tiled layout (RQ_X_TILED) or
     as FP6 tiles (RQ_X_FP6, bits 4)."""
     torch = _torch()
+    _check_2d(X, "X", (torch.float32, torch.float16, torch.bfloat16))
     M, K = X.shape
     cfg = make_cfg(bits, rot, x_layout=x_layout)
     if x_layout == RQ_X_ROWS:
@@ -224,24 +264,49 @@ def rotate_quantize(X, bits: int = 8, rot: int = 128, stream=None, x_layout: int
     return Xq, xs
 
 
+def _check_weights(Wq, w_scale, bias, N, K, cfg):
+    _check_vec(w_scale, "w_scale", N)
+    if bias is not None:
+        _check_vec(bias, "bias", N)
+    _check_bytes(Wq, "Wq", rq_weight_bytes(N, K, cfg), exact=True)
+
+
 def rotq_linear(X, Wq, w_scale, bias=None, bits: int = 8, rot: int = 128, workspace=None,
                 out=None, stream=None, w_layout: int = RQ_W_ROWS, act: int = RQ_ACT_NONE):
     """Y [M, N] = act(dequant(int GEMM(rotate+quantize(X), Wq)) + bias), in X's dtype;
     N = len(w_scale). w_layout must be the layout Wq was quantized in (RQ_W_FP6: the FP6
-    matrix-core path); act is RQ_ACT_NONE, RQ_ACT_GELU_ERF or RQ_ACT_GELU_TANH."""
+    matrix-core path); act is RQ_ACT_NONE, RQ_ACT_GELU_ERF or RQ_ACT_GELU_TANH. Shapes, dtypes
+    and buffer sizes are checked here (ValueError) because the C ABI only sees pointers."""
     torch = _torch()
+    _check_2d(X, "X", (torch.float16, torch.bfloat16))
     M, K = X.shape
-    N = w_scale.shape[0]
+    N = w_scale.shape[0] if w_scale.dim() == 1 else -1
     cfg = make_cfg(bits, rot, w_layout=w_layout, act=act)
+    _check_weights(Wq, w_scale, bias, N, K, cfg)
     need = rq_rotq_linear_workspace_size(M, K, cfg)
+    if workspace is not None:
+        _check_bytes(workspace, "workspace", need, exact=False)
+    if out is not None:
+        if tuple(out.shape) != (M, N) or out.dtype != X.dtype or not out.is_contiguous():
+            raise ValueError("out must be a contiguous %s tensor of shape (%d, %d), got %s %s"
+                             % (X.dtype, M, N, out.dtype, tuple(out.shape)))
+    _same_device(X, Wq, w_scale, bias, workspace, out)
     if workspace is None:
         workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=X.device)
     Y = torch.empty((M, N), dtype=X.dtype, device=X.device) if out is None else out
     _check(rq_rotq_linear(_dev(X, "X"), _dtype_code(X), M, K, _dev(Wq, "Wq"), _dev(w_scale, "w_scale"),
                           N, _dev(bias, "bias") if bias is not None else None, cfg, _dev(Y, "Y"),
-                          _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
-                          _stream(stream)), "rq_rotq_linear")
+                          _dev(workspace, "workspace"), _nbytes(workspace), _stream(stream)),
+           "rq_rotq_linear")
     return Y
+
+
+def _gemm_k(Wq, bits, K):
+    if K is not None:
+        return K
+    if Wq.dim() != 2:
+        raise ValueError("give K for a flat Wq buffer (FP6 weight tiles)")
+    return Wq.shape[1] if bits == 8 else 2 * Wq.shape[1]
 
 
 def gemm_dequant(Xq, x_scale, Wq, w_scale, bias=None, bits: int = 8, K: Optional[int] = None,
@@ -250,15 +315,21 @@ def gemm_dequant(Xq, x_scale, Wq, w_scale, bias=None, bits: int = 8, K: Optional
     """Y [M, N] from codes, after the epilogue activation act; M = len(x_scale),
     N = len(w_scale), K from Wq unless given (give K for FP6 weight tiles)."""
     torch = _torch()
-    M = x_scale.shape[0]
-    N = w_scale.shape[0]
-    K = K if K is not None else (Wq.shape[1] if bits == 8 else 2 * Wq.shape[1])
+    M = x_scale.shape[0] if x_scale.dim() == 1 else -1
+    N = w_scale.shape[0] if w_scale.dim() == 1 else -1
+    K = _gemm_k(Wq, bits, K)
+    cfg = make_cfg(bits, x_layout=x_layout, w_layout=w_layout, act=act)
+    _check_vec(x_scale, "x_scale", M)
+    _check_weights(Wq, w_scale, bias, N, K, cfg)
+    _check_bytes(Xq, "Xq", rq_codes_bytes(M, K, cfg), exact=False)
     out_dtype = torch.float16 if out_dtype is None else out_dtype
+    if out_dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("out_dtype must be float16 or bfloat16")
+    _same_device(Xq, x_scale, Wq, w_scale, bias)
     Y = torch.empty((M, N), dtype=out_dtype, device=Xq.device)
     _check(rq_gemm_dequant(_dev(Xq, "Xq"), _dev(x_scale, "x_scale"), _dev(Wq, "Wq"), _dev(w_scale, "w_scale"),
-                           _dev(bias, "bias") if bias is not None else None, M, N, K,
-                           make_cfg(bits, x_layout=x_layout, w_layout=w_layout, act=act), Y.data_ptr(), _dtype_code(Y),
-                           _stream(stream)), "rq_gemm_dequant")
+                           _dev(bias, "bias") if bias is not None else None, M, N, K, cfg, Y.data_ptr(),
+                           _dtype_code(Y), _stream(stream)), "rq_gemm_dequant")
     return Y
 
 
@@ -268,10 +339,20 @@ def gemm_s32(Xq, Wq, bits: int = 8, K: Optional[int] = None, stream=None,
     """acc [M, N] int32; M = Xq.shape[0] and N = Wq.shape[0] for row-major codes (give M for the
     tiled layouts, N and K for FP6 weight tiles)."""
     torch = _torch()
-    M = Xq.shape[0] if M is None else M
-    N = Wq.shape[0] if N is None else N
-    K = K if K is not None else (Wq.shape[1] if bits == 8 else 2 * Wq.shape[1])
+    if M is None:
+        if x_layout != RQ_X_ROWS or Xq.dim() != 2:
+            raise ValueError("give M for codes in a tiled layout")
+        M = Xq.shape[0]
+    if N is None:
+        if w_layout != RQ_W_ROWS or Wq.dim() != 2:
+            raise ValueError("give N for FP6 weight tiles")
+        N = Wq.shape[0]
+    K = _gemm_k(Wq, bits, K)
+    cfg = make_cfg(bits, x_layout=x_layout, w_layout=w_layout)
+    _check_bytes(Xq, "Xq", rq_codes_bytes(M, K, cfg), exact=False)
+    _check_bytes(Wq, "Wq", rq_weight_bytes(N, K, cfg), exact=True)
+    _same_device(Xq, Wq)
     acc = torch.empty((M, N), dtype=torch.int32, device=Xq.device)
-    _check(rq_gemm_s32(_dev(Xq, "Xq"), _dev(Wq, "Wq"), M, N, K, make_cfg(bits, x_layout=x_layout, w_layout=w_layout),
-                       acc.data_ptr(), _stream(stream)), "rq_gemm_s32")
+    _check(rq_gemm_s32(_dev(Xq, "Xq"), _dev(Wq, "Wq"), M, N, K, cfg, acc.data_ptr(), _stream(stream)),
+           "rq_gemm_s32")
     return acc

@@ -34,8 +34,9 @@
 //     tile instead (one 512-thread workgroup per CU, 146 KB LDS): two groups of four take the
 //     even and the odd k steps in lockstep, each with its own half of a doubled ring, then swap
 //     halves of their accumulators through LDS so that each wave finishes one 32-row block.
-//   * Launches with more tiles than CUs, int8 codes in the tiled layout, an fp16/bf16 output
-//     and K of 1024, 1536 or 2048 bytes load each wave's Xq fragments straight into registers
+//   * Launches with more tiles than CUs, int8 codes in the tiled layout and K of 1024, 1536
+//     or 2048 bytes (any output: fp16/bf16 or the raw int32 accumulators) load each wave's Xq
+//     fragments straight into registers
 //     instead (gemm_xr_kernel): a wave multiplies only its own 64 Xq rows, so only Wq, which
 //     the four waves share, goes through LDS.
 //   * Launches with more tiles than CUs and at least 48 k steps use 256 x 256 tiles instead:
@@ -555,7 +556,8 @@ __global__ __launch_bounds__(512, 1) void gemm_n2_kernel(
   tile_epilogue_act<BITS, OUT, 2>(act, acc, scales, lds + wave_all * (64 * 256), wave * 64, lane, m0, n0 + 128 * grp, M, N, Y);
 }
 
-// Xq fragments straight into registers (int8 codes, tiled Xq, output in fp16/bf16). In the
+// Xq fragments straight into registers (int8 codes, tiled Xq; output fp16/bf16, or the int32
+// accumulators for the same launches' bit-exact checks). In the
 // 256 x 128 tile each wave multiplies only its own 64 Xq rows, so staging Xq through LDS buys
 // no reuse: here each wave loads its two 32-row fragments per 32-byte slice with 16-byte global
 // loads (lane l: row l % 32, 16-byte chunk 2 s + l / 32 of the step), two k steps ahead in three
@@ -588,7 +590,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_xr_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   float my_sw = 0.0f, my_b = 0.0f, my_sx = 0.0f;
-  {
+  if constexpr (OUT != kOutS32) {
     const int n = n0 + (int)threadIdx.x, m = m0 + (int)threadIdx.x;
     if (threadIdx.x < kBN && n < N) {
       my_sw = sw[n];
@@ -660,7 +662,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_xr_kernel(
   load_x(1, xs[1]);
   __builtin_amdgcn_sched_barrier(0);
   vm_wait(std::integral_constant<int, 10>{});   // Wq of step 0 landed (10 loads issued after it)
-  {
+  if constexpr (OUT != kOutS32) {
     float* e_sw = reinterpret_cast<float*>(lds + kScalesOff);
     if (threadIdx.x < kBN) {
       e_sw[threadIdx.x] = my_sw;
@@ -745,7 +747,7 @@ hipError_t launch(const void* Xq, const float* sx, const void* Wq, const float* 
                        bias, Y, (int)M, (int)N, (int)Kb, tiles_m, tiles_n, act);
     return hipGetLastError();
   }
-  if constexpr (BITS == 8 && XT && OUT != kOutS32) {
+  if constexpr (BITS == 8 && XT) {
     if (ntiles > kNumCUs && (Kb == 1024 || Kb == 1536 || Kb == 2048)) {
       auto k = Kb == 1024 ? gemm_xr_kernel<OUT, 16> : Kb == 1536 ? gemm_xr_kernel<OUT, 24> : gemm_xr_kernel<OUT, 32>;
       hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), 0, st, static_cast<const uint8_t*>(Xq), sx,

@@ -136,9 +136,12 @@ __device__ __forceinline__ float wave_max(float a, int width) {
   return a;
 }
 
+// The row's multiplier and scale. A row whose absmax is zero, or too small for fl(q_max / a)
+// to be finite, is quantized as a zero row: multiplier 0 (every code 0) and scale 0.
 __device__ __forceinline__ void row_scalars(float a, float qmax, int j, float& tinv, float& scale) {
-  const float inv = (a > 0.0f) ? __fdiv_rn(qmax, a) : 0.0f;
-  scale = __fdiv_rn(__fmul_rn(a, kInvSqrtBlock), qmax);
+  float inv = (a > 0.0f) ? __fdiv_rn(qmax, a) : 0.0f;
+  if (__builtin_isinf(inv)) inv = 0.0f;
+  scale = inv != 0.0f ? __fdiv_rn(__fmul_rn(a, kInvSqrtBlock), qmax) : 0.0f;
   tinv = (__builtin_popcount(j) & 1) ? -inv : inv;
 }
 

@@ -112,12 +112,19 @@ __device__ __forceinline__ int64_t fp6w_offset(int64_t row, int s, int h, int b,
   return base + 128 * 32 + rr * 16 + 8 * (h ^ ((rr >> 4) & 1)) + (b - 16);
 }
 
-// Quantize one row against threshold t (t == 0: codes 0); returns the row's scale. BITS = 6
-// stores 4-bit codes as FP6 weight tiles.
+// The multiplier fl(q_max / t) of threshold t, or 0 -- the zero-row rule -- when t is 0 or too
+// small for the quotient to be finite.
+__device__ __forceinline__ float clip_inv(float t, float qmax) {
+  const float inv = t > 0.0f ? __fdiv_rn(qmax, t) : 0.0f;
+  return __builtin_isinf(inv) ? 0.0f : inv;
+}
+
+// Quantize one row against threshold t (t == 0, or a t whose multiplier overflows: codes 0 and
+// scale 0); returns the row's scale. BITS = 6 stores 4-bit codes as FP6 weight tiles.
 template <int DT, int BITS>
 __device__ float quantize_row(const void* X, int64_t row, int64_t K, float t, uint8_t* Q, int lane) {
   const float qmax = BITS == 8 ? 127.0f : 7.0f;
-  const float inv = t > 0.0f ? __fdiv_rn(qmax, t) : 0.0f;
+  const float inv = clip_inv(t, qmax);
   const int nb = static_cast<int>(K / 128);
   for (int b = 0; b < nb; b++) {
     float v0, v1;
@@ -143,7 +150,7 @@ __device__ float quantize_row(const void* X, int64_t row, int64_t K, float t, ui
       Q[row * (K / 2) + 64 * (int64_t)b + lane] = static_cast<uint8_t>((q0 & 0xF) | ((q1 & 0xF) << 4));
     }
   }
-  return t > 0.0f ? __fdiv_rn(__fmul_rn(t, kInvSqrtBlock), qmax) : 0.0f;
+  return inv != 0.0f ? __fdiv_rn(__fmul_rn(t, kInvSqrtBlock), qmax) : 0.0f;
 }
 
 template <int DT, int BITS>
@@ -161,8 +168,8 @@ __global__ __launch_bounds__(64) void mse_clip_kernel(const void* __restrict__ X
     // Candidate lane_i: t_i, inv_i, s_i exactly as the final quantization would use them.
     const int cand = lane < kNClip ? lane : 0;
     const float ti = __fmul_rn(a, __fdiv_rn(static_cast<float>(100 - cand), 100.0f));
-    const float inv = __fdiv_rn(qmax, ti);
-    const double sd = static_cast<double>(__fdiv_rn(__fmul_rn(ti, kInvSqrtBlock), qmax));
+    const float inv = clip_inv(ti, qmax);       // 0: this candidate quantizes the row to zero
+    const double sd = inv != 0.0f ? static_cast<double>(__fdiv_rn(__fmul_rn(ti, kInvSqrtBlock), qmax)) : 0.0;
     const double cd = static_cast<double>(kInvSqrtBlock);
     double e = 0.0;
     for (int b = 0; b < nb; b++) {
