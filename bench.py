@@ -96,20 +96,23 @@ def _read_counter_csv(path):
 
 
 def _is_gemm(kernel_name):
-    """The library's GEMM kernels: gemm_kernel, gemm_xr_kernel, gemm_n2_kernel, gemm_wide_kernel
-    and gemm_fp6_kernel (template arguments follow the name)."""
+    """The library's GEMM kernels: gemm_kernel, gemm_xr_kernel, gemm_rw_kernel, gemm_n2_kernel,
+    gemm_wide_kernel and gemm_fp6_kernel (template arguments follow the name)."""
     import re
     return re.search(r"(?:^|::|\s)gemm_\w*kernel\s*[<(]", kernel_name) is not None
 
 
 def gemm_kernel_name(M, N, K, bits, x_layout, w_layout=0, act=0, s32=False):
     """The GEMM kernel the launcher picks for a call, by the dispatch rule of gemm_i8.hip,
-    gemm_i8_wide.hip and gemm_fp6.hip (a label for the roofline record)."""
+    gemm_rw.hip, gemm_i8_wide.hip and gemm_fp6.hip (a label for the roofline record)."""
     from w4a4_integer_quantized_amd import binding as rq
     if w_layout == rq.RQ_W_FP6:
         return "gemm_fp6_kernel"
     Kb = K if bits == 8 else K // 2
     tiles = -(-M // 256) * -(-N // 128)
+    if bits == 8 and x_layout == rq.RQ_X_TILED and Kb == 1024 and N == 32 * 96 and -(-M // 64) >= 64 \
+            and -(-M // 256) * 256 * 1024 < 2 ** 31:
+        return "gemm_rw_kernel"
     if x_layout == rq.RQ_X_ROWS and act == 0 and 1536 <= Kb < 3072 and -(-M // 256) * -(-N // 256) >= 192:
         return "gemm_wide_kernel"
     if tiles <= 256 and (Kb // 64) % 2 == 0 and Kb // 64 >= 16:

@@ -98,6 +98,7 @@ def test_more_than_one_gpu_is_refused():
 
 def test_gemm_kernel_names_are_recognised():
     for name in (GEMM, "void convrot::(anonymous namespace)::gemm_xr_kernel<1, 16>(unsigned char const*)",
+                 "void convrot::(anonymous namespace)::gemm_rw_kernel<1, 96, 0>(unsigned char const*)",
                  "void convrot::(anonymous namespace)::gemm_n2_kernel<8, 2, true>(unsigned char const*)",
                  "convrot::(anonymous namespace)::gemm_wide_kernel<4, 1>(unsigned char const*)",
                  "void convrot::(anonymous namespace)::gemm_fp6_kernel<1, 1>(unsigned char const*)"):
@@ -110,7 +111,11 @@ def test_gemm_kernel_label_follows_the_launch_rule():
     from w4a4_integer_quantized_amd import binding as rq
     T, R = rq.RQ_X_TILED, rq.RQ_X_ROWS
     # The shapes the GPU parity tests send to each kernel.
-    assert bench.gemm_kernel_name(41472, 3072, 1024, 8, T) == "gemm_xr_kernel"
+    assert bench.gemm_kernel_name(41472, 3072, 1024, 8, T) == "gemm_rw_kernel"
+    assert bench.gemm_kernel_name(41472, 3072, 1024, 8, T, s32=True) == "gemm_rw_kernel"
+    assert bench.gemm_kernel_name(4033, 3072, 1024, 8, T) == "gemm_rw_kernel"
+    assert bench.gemm_kernel_name(4032, 3072, 1024, 8, T) == "gemm_xr_kernel"
+    assert bench.gemm_kernel_name(41472, 1024, 1024, 8, T) == "gemm_xr_kernel"
     assert bench.gemm_kernel_name(4100, 2064, 1024, 8, T) == "gemm_xr_kernel"
     assert bench.gemm_kernel_name(4100, 2064, 1024, 8, T, s32=True) == "gemm_xr_kernel"   # same kernel for int32
     assert bench.gemm_kernel_name(4100, 2064, 2048, 4, T) == "gemm_kernel"        # int4: Kb = 1024

@@ -274,6 +274,41 @@ def test_gemm_xr_choice_parity(M, N, K, bits, layout):
     assert np.array_equal(bits_from_dev(y_nb)[rows], oracle.epilogue(ref_acc, sx[rows], sw, None, IO_CODE["f16"]))
 
 
+# Shapes the launcher sends to the kernel with each CU's weight tile resident in LDS (int8 codes
+# in the tiled layout, K = 1024, N = 32 x 96, at least 64 token blocks of 64 per XCD-eighth):
+# the smallest such M, ragged M (a partial last block and a partial last 256-row panel), M just
+# below the threshold (the next kernel takes it), and several blocks per wave. Every element of
+# the int32 accumulators and of both output types is compared.
+RW_CASES = [(4096, 3072, 1024), (4100, 3072, 1024), (4033, 3072, 1024), (9999, 3072, 1024),
+            (4032, 3072, 1024)]
+
+
+@pytest.mark.parametrize("M,N,K", RW_CASES)
+def test_gemm_rw_choice_parity(M, N, K):
+    need_gpu()
+    print("rw-choice case M=%d N=%d K=%d" % (M, N, K), flush=True)
+    rng = np.random.default_rng(M + 7 * N + K)
+    A = _random_codes(rng, M, K, 8)
+    B = _random_codes(rng, N, K, 8)
+    Ad = torch.from_numpy(tile_codes(oracle.pack_codes(A, 8), M, K, 8, pad_fill=0x7F)).cuda()
+    Bd = torch.from_numpy(oracle.pack_codes(B, 8)).cuda()
+    sx = (rng.random(M) * 0.05).astype(np.float32)
+    sw = (rng.random(N) * 2e-4).astype(np.float32)
+    b = rng.normal(0, 0.01, N).astype(np.float32)
+    dev = lambda a: torch.from_numpy(a).cuda()
+    acc = rq.gemm_s32(Ad, Bd, bits=8, K=K, x_layout=rq.RQ_X_TILED, M=M)
+    ys = {io: rq.gemm_dequant(Ad, dev(sx), Bd, dev(sw), dev(b), bits=8, K=K, x_layout=rq.RQ_X_TILED,
+                              out_dtype=torch.float16 if io == "f16" else torch.bfloat16)
+          for io in ("f16", "bf16")}
+    y_nb = rq.gemm_dequant(Ad, dev(sx), Bd, dev(sw), None, bits=8, K=K, x_layout=rq.RQ_X_TILED)
+    torch.cuda.synchronize()
+    ref_acc = oracle.gemm_s32(A, B)
+    assert np.array_equal(acc.cpu().numpy(), ref_acc)
+    for io, Y in ys.items():
+        assert np.array_equal(bits_from_dev(Y), oracle.epilogue(ref_acc, sx, sw, b, IO_CODE[io])), io
+    assert np.array_equal(bits_from_dev(y_nb), oracle.epilogue(ref_acc, sx, sw, None, IO_CODE["f16"]))
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 32784, 1024), (300, 16400, 2048), (64, 32784, 1536)])
 def test_gemm_xr_few_rows_many_tiles(M, N, K):
     """Xq fragments in registers with one or two token panels spread over more tiles than CUs:
@@ -403,9 +438,14 @@ def test_runtime_errors_are_raised():
     ws = torch.zeros(32, dtype=torch.float32, device="cuda")
     X = torch.zeros(16, 128, dtype=torch.float16, device="cuda")
     small = torch.empty(64, dtype=torch.uint8, device="cuda")
-    with pytest.raises(rq.ConvRotError) as e:
+    with pytest.raises(ValueError):                 # the wrapper checks the size first
         rq.rotq_linear(X, Wq, ws, workspace=small)
-    assert e.value.status == rq.RQ_EWORKSPACE
+    # The C entry point itself returns RQ_EWORKSPACE for the same call.
+    Y = torch.empty((16, 32), dtype=torch.float16, device="cuda")
+    st = rq.rq_rotq_linear(X.data_ptr(), rq.RQ_F16, 16, 128, Wq.data_ptr(), ws.data_ptr(), 32, None,
+                           rq.make_cfg(8), Y.data_ptr(), small.data_ptr(), 64,
+                           torch.cuda.current_stream().cuda_stream)
+    assert st == rq.RQ_EWORKSPACE
 
 
 def _edge_rows(K, io, bits):

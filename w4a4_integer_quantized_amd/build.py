@@ -24,7 +24,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
-SOURCES = ["rotate_quant.hip", "gemm_i8.hip", "gemm_i8_wide.hip", "gemm_fp6.hip", "weight_quant.hip", "api.hip"]
+SOURCES = ["rotate_quant.hip", "gemm_i8.hip", "gemm_rw.hip", "gemm_i8_wide.hip", "gemm_fp6.hip", "weight_quant.hip", "api.hip"]
 
 
 def _compile(src: str) -> str:

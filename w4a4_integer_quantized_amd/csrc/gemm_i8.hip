@@ -799,6 +799,8 @@ hipError_t launch_gemm(const void* Xq, const float* sx, const void* Wq, const fl
   // traffic per MFMA measured faster (by up to ~20%) than 64-byte row segments; from 3072 bytes
   // on, the eight-wave 256 x 256 kernel here measured faster still (by ~15%).
   // The 128-byte-row kernel has no activation variant; with one, the 64-byte-row kernels run.
+  if (x_tiled && gemm_rw_supported(M, N, Kb, bits, x_tiled))
+    return launch_gemm_rw(Xq, sx, Wq, sw, bias, M, N, Y, out_dt, acc32, act, stream);
   if (x_tiled)
     return launch_layout<true>(Xq, sx, Wq, sw, bias, M, N, Kb, bits, Y, out_dt, acc32, act, stream);
   const int64_t wide_tiles = ((M + 255) / 256) * ((N + 255) / 256);

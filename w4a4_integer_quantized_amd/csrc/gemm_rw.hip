@@ -1,0 +1,326 @@
+// gemm_rw.hip -- int8 GEMM with the weight tile resident in LDS and eight independent waves.
+//
+// The same product and epilogue as gemm_i8.hip (acc[m, n] = sum_k Xq[m, k] * Wq[n, k] in int32,
+// Y = fp16/bf16(fma(f32(acc), fl(w_scale[n] * x_scale[m]), bias[n]))): the W8A8 operations of
+// the "SAM 3.1 Multiplex INT8/INT4 ConvRot" page ("Quantization recipe"), per-row weight scale
+// and per-token activation scale. This kernel serves int8 codes with K = 1024 in the tiled
+// activation layout, on launches with many 64-token blocks per output tile.
+//
+// Design (gfx950: 256 CUs in 8 XCDs of 32, 160 KB LDS per CU, 4 SIMDs per CU):
+//   * One 512-thread workgroup per CU. The workgroup owns BN output features (an "n-tile")
+//     for its whole life: their weight rows, all of K, are copied into LDS once (BN * 1 KB,
+//     96 or 128 KB) in MFMA-fragment order, so every fragment read is one contiguous 1 KB block.
+//     w_scale and bias for the n-tile are parked next to them.
+//   * Each of the eight waves then walks its own sequence of 64-token blocks: it streams those
+//     tokens' codes from global memory straight into registers (2 k steps ahead), multiplies
+//     them against the resident weights with v_mfma_i32_16x16x64_i8 (A = 16 weight rows,
+//     B = 16 tokens, both 64 bytes of K per lane group), and finishes each block with its own
+//     epilogue through a private LDS staging area. No barrier follows the initial copy: the two
+//     waves on each SIMD run unsynchronized, so one's epilogue overlaps the other's matrix work.
+//   * With the 16 x 16 x 64 operand layout (lane l: row l % 16, bytes 16 (l / 16) .. +16 of a
+//     64-byte k step) a 16-token fragment is 16 rows x 64 B, one contiguous 1 KB block of the
+//     tiled activation layout, so each fragment load moves whole cache lines.
+//   * Work map: workgroup b runs on XCD b % 8 (round-robin dispatch). The 32 workgroups of an
+//     XCD split into NT n-tiles x G row groups (NT * G = 32); XCD x takes the x-th eighth of the
+//     token blocks, split G ways. All workgroups of an XCD thus read the same token blocks at
+//     about the same time, and each block of codes comes from HBM once per XCD and then from
+//     that XCD's L2.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "gemm_common.h"
+#include "internal.h"
+
+namespace convrot {
+namespace {
+
+using namespace gemm;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kRwThreads = 512;
+constexpr int kRwWaves = 8;
+constexpr int kRwRows = 64;            // tokens per wave tile
+constexpr int kRwDepth = 2;            // k steps of codes in flight ahead of the MFMAs
+constexpr int kRwSets = 4;             // register sets of codes (a power of two > kRwDepth)
+
+// Epilogue staging, per wave: BN = 96 stages 16 tokens x 96 features per round in 256-byte
+// rows (16-byte chunk c of row r at position c ^ r); BN = 128 stages 16 tokens x 64 features
+// per round in 128-byte rows (position c ^ ((r >> 1) & 7)). Under gfx950's LDS bank model
+// (64 banks of 4 bytes, address bit 9 folded into bank bit 5) both make the 8-byte writes of
+// 32 lanes and the 16-byte reads of 16 lanes conflict free.
+template <int BN> struct RwShape {
+  static constexpr int NA = BN / 16;                       // 16-row weight blocks
+  static constexpr int kCols = BN == 96 ? 96 : 64;         // features per staging round
+  static constexpr int kPitch = BN == 96 ? 256 : 128;      // staged row pitch in bytes
+  static constexpr int kRounds = BN / kCols;               // column rounds per 16-token block
+  static constexpr int kLanesPerRow = kPitch / 16;         // lanes per staged row on readback
+  static constexpr int kStage = 16 * kPitch;               // bytes per wave
+  static constexpr int kWq = BN * 1024;                    // resident weights (K = 1024)
+  static constexpr int kLds = kWq + kRwWaves * kStage + 2 * BN * 4;
+};
+
+template <int BN>
+__device__ __forceinline__ int stage_pos(int c, int r) {
+  if constexpr (BN == 96) return c ^ r;
+  return c ^ ((r >> 1) & 7);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rw_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// NT n-tiles per XCD times G row groups = 32 workgroups per XCD; rb_total 64-token blocks.
+// The per-wave loop body (16 k steps and the epilogue) is one basic block: stores and the
+// x_scale loads are buffer operations whose out-of-range lanes the hardware drops (stores) or
+// zero-fills (loads), and the activation is a template parameter. With no branch inside,
+// code generation cannot sink the next block's look-ahead loads below the MFMAs that hide
+// them.
+template <int OUT, int BN, int ACT>
+__global__ __launch_bounds__(kRwThreads, 1) void gemm_rw_kernel(
+    const uint8_t* __restrict__ Xq, const float* __restrict__ sx, const uint8_t* __restrict__ Wq,
+    const float* __restrict__ sw, const float* __restrict__ bias, void* __restrict__ Y, int M,
+    int N, int NT, int G, int rb_total, uint32_t xq_bytes) {
+  using S = RwShape<BN>;
+  constexpr int NA = S::NA;
+  constexpr int NK = 16;                 // 64-byte k steps (K = 1024)
+  constexpr int Kb = NK * 64;
+  constexpr int kOutBytes = OUT == kOutS32 ? 4 : 2;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[S::kLds];
+  float* const e_sw = reinterpret_cast<float*>(lds + S::kWq + kRwWaves * S::kStage);
+  float* const e_b = e_sw + BN;
+
+  const int xcd = blockIdx.x & 7;
+  const int c = blockIdx.x >> 3;
+  const int nt = c % NT, g = c / NT;
+  const int n0 = nt * BN;
+  const int parts = 8 * G, part = xcd * G + g;
+  const int rb_lo = (int)((int64_t)rb_total * part / parts);
+  const int rb_hi = (int)((int64_t)rb_total * (part + 1) / parts);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  // 1. The n-tile's weights into LDS, fragment f = kk * NA + a at f * 1 KB: lane l holds row
+  //    n0 + 16 a + l % 16, bytes 64 kk + 16 (l / 16) .. +16. Rows past N re-read the last row.
+  {
+    const int wrows = N - n0 < BN ? N - n0 : BN;
+    const __amdgpu_buffer_rsrc_t wrs = rw_rsrc(Wq + (int64_t)n0 * Kb, (uint32_t)wrows * Kb);
+    constexpr int kFrags = NA * NK;
+    static_assert(kFrags % kRwWaves == 0, "whole fragments per wave");
+#pragma unroll
+    for (int i = 0; i < kFrags / kRwWaves; i++) {
+      const int f = wave + kRwWaves * i;
+      const int kk = f / NA, a = f - kk * NA;
+      int r = a * 16 + (lane & 15);
+      r = r < wrows ? r : wrows - 1;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (lds_void*)(lds + f * 1024), 16,
+                                               r * Kb + kk * 64 + (lane >> 4) * 16, 0, 0, 0);
+    }
+    if constexpr (OUT != kOutS32) {
+      if ((int)threadIdx.x < BN) {
+        const int n = n0 + (int)threadIdx.x;
+        e_sw[threadIdx.x] = n < N ? sw[n] : 0.0f;
+        e_b[threadIdx.x] = (n < N && bias) ? bias[n] : 0.0f;
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  // 2. This wave's token blocks: rb_lo + wave, + 8, ...
+  int rb = rb_lo + wave;
+  if (rb >= rb_hi) return;
+  const __amdgpu_buffer_rsrc_t xrs = rw_rsrc(Xq, xq_bytes);
+  const __amdgpu_buffer_rsrc_t srs = rw_rsrc(sx, (uint32_t)M * 4u);
+  // Lane offset within a 16-token fragment of the tiled layout (row l % 16, chunk l / 16).
+  const int xlane = ((lane & 15) << 6) + ((lane >> 4) << 4);
+  // Byte offset of block b's k step 0 (panel b / 4, quarter b % 4).
+  auto block_base = [](int b) { return (int)((((b >> 2) * NK) << 14) + ((b & 3) << 12)); };
+  auto load_step = [&](int base, int kk, v4i (&x)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int b = 0; b < 4; b++)
+      x[b] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(xrs, xlane + (b << 10),
+                                                                          base + (kk << 14), 0));
+  };
+  auto read_w = [&](int kk, int a) __attribute__((always_inline)) {
+    return *reinterpret_cast<const v4i*>(lds + (kk * NA + a) * 1024 + lane * 16);
+  };
+
+  v4i xs[kRwSets][4];
+  v4i wf[NA];
+  v4i acc[NA][4];
+  int base = block_base(rb);
+#pragma unroll
+  for (int s = 0; s < kRwDepth; s++) load_step(base, s, xs[s]);
+#pragma unroll
+  for (int a = 0; a < NA; a++) wf[a] = read_w(0, a);
+  uint8_t* const stage = lds + S::kWq + wave * S::kStage;
+  const int r16 = lane & 15;               // token within a 16-token block (staging row)
+  const int hq = lane >> 4;                // which 4 features of a 16-row weight block
+
+  // One 64-token block: 16 k steps, then the epilogue. The first block is peeled off the loop
+  // so that both paths into the loop arrive with the previous epilogue's stores in flight;
+  // the compiler's wait counts at the loop head then let those stores drain under the
+  // first k steps instead of before them.
+  auto block = [&](int rb) __attribute__((always_inline)) {
+    // The next block (this one again after the last: harmless in-bounds look-ahead loads).
+    const int rb_next = rb + kRwWaves;
+    const int base_next = block_base(rb_next < rb_hi ? rb_next : rb);
+    const int m_base = rb * kRwRows;
+    // x_scale of this block's tokens for the epilogue (lane: token 16 b + l % 16; zero past M).
+    float xsc[4];
+    if constexpr (OUT != kOutS32) {
+#pragma unroll
+      for (int b = 0; b < 4; b++)
+        xsc[b] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                               srs, (m_base + b * 16 + r16) * 4, 0, 0));
+    }
+    // k step kk: issue the code loads of step kk + 2 (of the next block in the last two
+    // steps), then the 4 NA MFMAs of step kk, each weight fragment re-read for step kk + 1
+    // right after its last MFMA of this step. The schedule is pinned: the scheduler may not
+    // move the loads across steps, and each DS read follows its block's four MFMAs.
+#pragma unroll
+    for (int kk = 0; kk < NK; kk++) {
+      const int ahead = kk + kRwDepth;
+      if (ahead < NK) {
+        load_step(base, ahead, xs[ahead & (kRwSets - 1)]);
+      } else {
+        load_step(base_next, ahead - NK, xs[ahead & (kRwSets - 1)]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const v4i(&x)[4] = xs[kk & (kRwSets - 1)];
+#pragma unroll
+      for (int a = 0; a < NA; a++) {
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+          const v4i c0 = kk == 0 ? v4i{0, 0, 0, 0} : acc[a][b];
+          acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[a], x[b], c0, 0, 0, 0);
+        }
+        wf[a] = read_w((kk + 1) & (NK - 1), a);
+      }
+#pragma unroll
+      for (int a = 0; a < NA; a++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);     // 4 MFMAs of block a
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // its DS read for step kk + 1
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // Epilogue. Lane l holds, for block (a, b), D[n][m] at n = 16 a + 4 (l / 16) + e (e = 0..3)
+    // and token m = 16 b + l % 16. Outputs go through a buffer resource that starts at this
+    // block's first token and holds only its valid tokens, so stores past M are dropped.
+    const int rows_valid = M - m_base < kRwRows ? M - m_base : kRwRows;
+    const __amdgpu_buffer_rsrc_t yrs =
+        rw_rsrc(static_cast<uint8_t*>(Y) + (int64_t)m_base * N * kOutBytes, (uint32_t)(rows_valid * N * kOutBytes));
+    if constexpr (OUT == kOutS32) {
+#pragma unroll
+      for (int b = 0; b < 4; b++)
+#pragma unroll
+        for (int a = 0; a < NA; a++) {
+          const int n = n0 + a * 16 + 4 * hq;
+          const int off = n < N ? ((b * 16 + r16) * N + n) * 4 : (int)0x80000000;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[a][b]), yrs, off, 0, 0);
+        }
+    } else {
+      // Streaming (nontemporal) stores without an activation: Y is not re-read here. An
+      // activated output is the next linear's input and is stored normally (gemm_common.h).
+      constexpr int kStoreAux = ACT == kActNone ? 2 : 0;      // bit 1: nt
+#pragma unroll
+      for (int b = 0; b < 4; b++) {
+#pragma unroll
+        for (int rd = 0; rd < S::kRounds; rd++) {
+          // Convert and stage features [rd * kCols, (rd + 1) * kCols) of tokens 16 b .. +15.
+#pragma unroll
+          for (int aa = 0; aa < S::kCols / 16; aa++) {
+            const int a = rd * (S::kCols / 16) + aa;
+            const int col = a * 16 + 4 * hq;      // n-tile feature of element 0
+            const float4 s4 = *reinterpret_cast<const float4*>(e_sw + col);
+            const float4 b4 = *reinterpret_cast<const float4*>(e_b + col);
+            const float ws[4] = {s4.x, s4.y, s4.z, s4.w};
+            const float bs[4] = {b4.x, b4.y, b4.z, b4.w};
+            float y[4];
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+              y[e] = activate<ACT>(
+                  __builtin_fmaf(static_cast<float>(acc[a][b][e]), __fmul_rn(ws[e], xsc[b]), bs[e]));
+            uint2 o;
+            o.x = pack2(y[0], y[1], OUT);
+            o.y = pack2(y[2], y[3], OUT);
+            const int cc = 2 * aa + (hq >> 1);    // 16-byte chunk of the staged row
+            *reinterpret_cast<uint2*>(stage + r16 * S::kPitch + stage_pos<BN>(cc, r16) * 16 + (hq & 1) * 8) = o;
+          }
+          // Read back whole row segments and store them (a wave's LDS operations complete in
+          // order, so the reads see the writes above).
+          constexpr int kLpr = S::kLanesPerRow;
+          constexpr int kRowsPerIt = 64 / kLpr;
+          constexpr int kChunks = S::kCols / 8;   // 16-byte chunks holding data per row
+          u32x4 v[16 / kRowsPerIt];
+#pragma unroll
+          for (int it = 0; it < 16 / kRowsPerIt; it++) {
+            const int rr = it * kRowsPerIt + lane / kLpr;
+            const int j = lane % kLpr;
+            v[it] = *reinterpret_cast<const u32x4*>(stage + rr * S::kPitch + stage_pos<BN>(j, rr) * 16);
+          }
+#pragma unroll
+          for (int it = 0; it < 16 / kRowsPerIt; it++) {
+            const int rr = it * kRowsPerIt + lane / kLpr;
+            const int j = lane % kLpr;
+            const int n = n0 + rd * S::kCols + j * 8;
+            const int off = (j < kChunks && n < N) ? ((b * 16 + rr) * N + n) * 2 : (int)0x80000000;
+            __builtin_amdgcn_raw_buffer_store_b128(v[it], yrs, off, 0, kStoreAux);
+          }
+        }
+      }
+    }
+    return base_next;
+  };
+  base = block(rb);
+  for (rb += kRwWaves; rb < rb_hi; rb += kRwWaves) base = block(rb);
+}
+
+template <int OUT, int BN>
+hipError_t launch_bn(const void* Xq, const float* sx, const void* Wq, const float* sw,
+                     const float* bias, int64_t M, int64_t N, void* Y, int act, hipStream_t st) {
+  const int NT = (int)((N + BN - 1) / BN);
+  const int G = 32 / NT;
+  const int rb_total = (int)((M + kRwRows - 1) / kRwRows);
+  const int64_t xq_bytes = (M + 255) / 256 * 256 * 1024;
+  auto k = act == kActGeluErf ? gemm_rw_kernel<OUT, BN, kActGeluErf>
+         : act == kActGeluTanh ? gemm_rw_kernel<OUT, BN, kActGeluTanh>
+                               : gemm_rw_kernel<OUT, BN, kActNone>;
+  if constexpr (OUT == kOutS32) k = gemm_rw_kernel<OUT, BN, kActNone>;
+  hipLaunchKernelGGL(k, dim3(8 * NT * G), dim3(kRwThreads), 0, st, static_cast<const uint8_t*>(Xq), sx,
+                     static_cast<const uint8_t*>(Wq), sw, bias, Y, (int)M, (int)N, NT, G, rb_total,
+                     (uint32_t)xq_bytes);
+  return hipGetLastError();
+}
+
+// The n-tile width this kernel uses for N output features, or 0 when it does not take N: 96
+// when N is 32 tiles of 96 (one n-tile per CU of an XCD).
+int rw_tile(int64_t N) { return N == 32 * 96 ? 96 : 0; }
+
+}  // namespace
+
+bool gemm_rw_supported(int64_t M, int64_t N, int64_t Kb, int bits, bool x_tiled) {
+  if (bits != 8 || !x_tiled || Kb != 1024) return false;
+  const int bn = rw_tile(N);
+  if (bn == 0) return false;
+  const int64_t nt = (N + bn - 1) / bn, groups = 32 / nt;
+  const int64_t rb_total = (M + kRwRows - 1) / kRwRows;
+  // Every wave needs at least one token block of its own; the tiled codes and each block's
+  // outputs must fit 32-bit buffer offsets.
+  if (rb_total < 8 * groups * kRwWaves) return false;
+  return (M + 255) / 256 * 256 * 1024 < (int64_t(1) << 31) && kRwRows * N * 4 < (int64_t(1) << 31);
+}
+
+hipError_t launch_gemm_rw(const void* Xq, const float* sx, const void* Wq, const float* sw,
+                          const float* bias, int64_t M, int64_t N, void* Y, int out_dt,
+                          int32_t* acc32, int act, hipStream_t stream) {
+  if (acc32) return launch_bn<kOutS32, 96>(Xq, sx, Wq, sw, bias, M, N, acc32, act, stream);
+  if (out_dt == kF16) return launch_bn<kOutF16, 96>(Xq, sx, Wq, sw, bias, M, N, Y, act, stream);
+  return launch_bn<kOutBF16, 96>(Xq, sx, Wq, sw, bias, M, N, Y, act, stream);
+}
+
+}  // namespace convrot

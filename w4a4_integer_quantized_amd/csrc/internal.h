@@ -42,6 +42,14 @@ hipError_t launch_gemm_fp6(const void* Xt, const float* sx, const void* Wt, cons
                            const float* bias, int64_t M, int64_t N, int64_t K, void* Y,
                            int out_dt, int32_t* acc32, int act, hipStream_t stream);
 
+// The same GEMM with each CU's weight tile resident in LDS and eight independent waves
+// (int8 codes in the tiled layout, K = 1024; gemm_rw.hip). launch_gemm takes it where
+// gemm_rw_supported() holds.
+bool gemm_rw_supported(int64_t M, int64_t N, int64_t Kb, int bits, bool x_tiled);
+hipError_t launch_gemm_rw(const void* Xq, const float* sx, const void* Wq, const float* sw,
+                          const float* bias, int64_t M, int64_t N, void* Y, int out_dt,
+                          int32_t* acc32, int act, hipStream_t stream);
+
 // The same GEMM on 256 x 256 tiles with 128-byte k steps (launch_gemm picks it for long K);
 // it needs Kb (K in bytes of codes) to be a multiple of 128 and at least 256.
 bool wide_gemm_supported(int64_t Kb);
