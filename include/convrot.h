@@ -50,8 +50,9 @@
  *
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers, row-major, owned by the caller. The library
- *     allocates nothing and keeps no state between calls; it is safe to call from several host
- *     threads as long as concurrent calls do not share output buffers or workspaces.
+ *     allocates nothing and keeps no state between calls (apart from the static scratch of
+ *     rq_rotq_linear_noalloc, below); it is safe to call from several host threads as long as
+ *     concurrent calls do not share output buffers or workspaces.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default stream). Outputs are
  *     valid once the stream has been synchronized. Inputs must stay alive until then.
  *   - Every argument is validated on the host BEFORE any launch; a failed check launches nothing
@@ -186,6 +187,24 @@ rq_status rq_rotq_linear(const void *X, int32_t x_dtype, int64_t M, int64_t K,
                          const void *Wq, const float *w_scale, int64_t N, const float *bias,
                          const rq_qconfig *cfg, void *Y, void *workspace, size_t ws_bytes,
                          void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): rq_rotq_linear without a workspace argument. The
+ * workspace is a static device array of RQ_NOALLOC_SCRATCH_BYTES inside the library, one per
+ * GPU, held until the process ends; its address is looked up (hipGetSymbolAddress) on the first
+ * call on each device, with that device current. The call allocates nothing and runs the same
+ * kernels as rq_rotq_linear, on the current device (`stream` must belong to it).
+ *   Limit: rq_rotq_linear_workspace_size(M, K, cfg) <= RQ_NOALLOC_SCRATCH_BYTES (64 MiB: every
+ *   workload shape here, e.g. 41472 x 1024 or 8192 x 6144 8-bit codes); a larger call returns
+ *   RQ_EWORKSPACE and launches nothing.
+ *   Every call on one GPU shares that GPU's array, which keeps the last call's contents:
+ *   calls that overlap in time on one GPU (several host threads or streams) race. Nothing in
+ *   it needs to start at zero (each call writes all it reads).
+ * Other arguments, layouts, statuses and the output: as rq_rotq_linear. */
+#define RQ_NOALLOC_SCRATCH_BYTES (64u << 20)
+rq_status rq_rotq_linear_noalloc(const void *X, int32_t x_dtype, int64_t M, int64_t K,
+                                 const void *Wq, const float *w_scale, int64_t N,
+                                 const float *bias, const rq_qconfig *cfg, void *Y, void *stream);
 
 /* The GEMM + epilogue alone (the second kernel of rq_rotq_linear).
  *   Xq codes of M rows in cfg->x_layout (as rq_rotate_quantize writes them), x_scale [M];

@@ -275,3 +275,14 @@ def test_wrappers_accept_valid_cpu_buffers_up_to_the_device_check():
     Xt = torch.zeros(256 * 256, dtype=torch.uint8)
     with pytest.raises(ValueError, match="device tensor"):
         rq.gemm_s32(Xt, Wq, x_layout=rq.RQ_X_TILED, M=64)
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define RQ_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == rq.RQ_NOALLOC_SCRATCH_BYTES
+    # every workload's workspace fits it
+    from w4a4_integer_quantized_amd import synth
+    for cfg in synth.CONFIGS.values():
+        for lin in cfg.linears:
+            assert rq.workspace_size(cfg.M, lin.K, cfg.bits) <= rq.RQ_NOALLOC_SCRATCH_BYTES, (cfg.key, lin.name)

@@ -63,6 +63,7 @@ def load():
         "rq_quantize_weights": [P, I32, I64, I64, CFG, P, P, P],
         "rq_rotate_quantize": [P, I32, I64, I64, CFG, P, P, P],
         "rq_rotq_linear": [P, I32, I64, I64, P, P, I64, P, CFG, P, P, SZ, P],
+        "rq_rotq_linear_noalloc": [P, I32, I64, I64, P, P, I64, P, CFG, P, P],
         "rq_gemm_dequant": [P, P, P, P, P, I64, I64, I64, CFG, P, I32, P],
         "rq_gemm_s32": [P, P, I64, I64, I64, CFG, P, P],
         "rq_check_rotq_linear_args": [P, I32, I64, I64, P, P, I64, P, CFG, P, P, SZ],
@@ -117,6 +118,13 @@ def rq_rotate_quantize(X, x_dtype, M, K, cfg, Xq, x_scale, stream) -> int:
 def rq_rotq_linear(X, x_dtype, M, K, Wq, w_scale, N, bias, cfg, Y, ws, ws_bytes, stream) -> int:
     return load().rq_rotq_linear(X, x_dtype, M, K, Wq, w_scale, N, bias, ctypes.byref(cfg), Y, ws,
                                  ws_bytes, stream)
+
+
+RQ_NOALLOC_SCRATCH_BYTES = 64 << 20     # the static scratch of rq_rotq_linear_noalloc (convrot.h)
+
+
+def rq_rotq_linear_noalloc(X, x_dtype, M, K, Wq, w_scale, N, bias, cfg, Y, stream) -> int:
+    return load().rq_rotq_linear_noalloc(X, x_dtype, M, K, Wq, w_scale, N, bias, ctypes.byref(cfg), Y, stream)
 
 
 def rq_gemm_dequant(Xq, x_scale, Wq, w_scale, bias, M, N, K, cfg, Y, y_dtype, stream) -> int:

@@ -2,12 +2,14 @@
 //
 // Host side only: argument validation (a pure function of the arguments, no HIP call),
 // workspace carving, and the launches of the two kernels on the caller's stream. Nothing is
-// allocated and no state is kept between calls.
+// allocated. The only state is rq_rotq_linear_noalloc's static device scratch and the per-device
+// cache of its address.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "convrot.h"
@@ -140,9 +142,10 @@ rq_status check_rotate_args(const void* X, int32_t dt, int64_t rows, int64_t K, 
   return ok();
 }
 
-rq_status check_linear(const void* X, int32_t x_dtype, int64_t M, int64_t K, const void* Wq,
-                       const float* w_scale, int64_t N, const float* bias, const rq_qconfig* cfg,
-                       const void* Y, const void* ws, size_t ws_bytes) {
+// Everything of rq_rotq_linear's arguments but the workspace (M == 0 passes here).
+rq_status check_linear_core(const void* X, int32_t x_dtype, int64_t M, int64_t K, const void* Wq,
+                            const float* w_scale, int64_t N, const float* bias,
+                            const rq_qconfig* cfg, const void* Y) {
   rq_status s = check_cfg(cfg);
   if (s) return s;
   if (x_dtype != RQ_F16 && x_dtype != RQ_BF16)
@@ -155,17 +158,86 @@ rq_status check_linear(const void* X, int32_t x_dtype, int64_t M, int64_t K, con
   if ((s = check_ptr(w_scale, "w_scale"))) return s;
   if ((s = check_ptr(bias, "bias", false))) return s;
   if ((s = check_ptr(Y, "Y"))) return s;
-  if ((s = check_ptr(ws, "workspace"))) return s;
+  const int64_t xb = M * K * 2, wb = w_code_bytes(N, K, cfg->bits, cfg->w_layout), yb = M * N * 2;
+  if (overlap(Y, yb, X, xb) || overlap(Y, yb, Wq, wb) || overlap(Y, yb, w_scale, N * 4) ||
+      overlap(Y, yb, bias, N * 4))
+    return fail(RQ_EINVAL, "Y overlaps an input");
+  return ok();
+}
+
+// The workspace part: size, alignment and no overlap with the other buffers (M > 0).
+rq_status check_linear_ws(const void* X, int64_t M, int64_t K, const void* Wq, const float* w_scale,
+                          int64_t N, const float* bias, const rq_qconfig* cfg, const void* Y,
+                          const void* ws, size_t ws_bytes) {
+  rq_status s = check_ptr(ws, "workspace");
+  if (s) return s;
   const size_t need = rq_rotq_linear_workspace_size(M, K, cfg);
   if (ws_bytes < need)
     return fail(RQ_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
   const int64_t xb = M * K * 2, wb = w_code_bytes(N, K, cfg->bits, cfg->w_layout), yb = M * N * 2;
-  if (overlap(Y, yb, X, xb) || overlap(Y, yb, Wq, wb) || overlap(Y, yb, ws, (int64_t)need) ||
-      overlap(Y, yb, w_scale, N * 4) || overlap(Y, yb, bias, N * 4))
-    return fail(RQ_EINVAL, "Y overlaps an input or the workspace");
+  if (overlap(Y, yb, ws, (int64_t)need))
+    return fail(RQ_EINVAL, "Y overlaps the workspace");
   if (overlap(ws, (int64_t)need, X, xb) || overlap(ws, (int64_t)need, Wq, wb) ||
       overlap(ws, (int64_t)need, w_scale, N * 4) || overlap(ws, (int64_t)need, bias, N * 4))
     return fail(RQ_EINVAL, "workspace overlaps an input");
+  return ok();
+}
+
+rq_status check_linear(const void* X, int32_t x_dtype, int64_t M, int64_t K, const void* Wq,
+                       const float* w_scale, int64_t N, const float* bias, const rq_qconfig* cfg,
+                       const void* Y, const void* ws, size_t ws_bytes) {
+  rq_status s = check_linear_core(X, x_dtype, M, K, Wq, w_scale, N, bias, cfg, Y);
+  if (s || M == 0) return s;
+  return check_linear_ws(X, M, K, Wq, w_scale, N, bias, cfg, Y, ws, ws_bytes);
+}
+
+// The two kernels of the quantized linear on an already validated call; `workspace` holds at
+// least rq_rotq_linear_workspace_size(M, K, cfg) bytes.
+rq_status launch_linear(const void* X, int32_t x_dtype, int64_t M, int64_t K, const void* Wq,
+                        const float* w_scale, int64_t N, const float* bias, const rq_qconfig* cfg,
+                        void* Y, void* workspace, hipStream_t st) {
+  // The workspace holds the codes in the tiled layout (FP6 tiles with FP6 weights), then x_scale.
+  const int32_t xl = fused_x_layout(cfg);
+  uint8_t* Xq = static_cast<uint8_t*>(workspace);
+  float* sx = reinterpret_cast<float*>(Xq + round256(x_code_bytes(M, K, cfg->bits, xl)));
+  rq_status s;
+  if ((s = from_hip(convrot::launch_rotate_quant(X, x_dtype, M, K, cfg->bits, code_layout(xl), Xq, sx, st),
+                    "rotate_quant launch")))
+    return s;
+  if (xl == RQ_X_FP6)
+    return from_hip(convrot::launch_gemm_fp6(Xq, sx, Wq, w_scale, bias, M, N, K, Y, x_dtype, nullptr,
+                                             cfg->act, st),
+                    "gemm launch");
+  return from_hip(convrot::launch_gemm(Xq, sx, Wq, w_scale, bias, M, N, K, cfg->bits, true, Y,
+                                       x_dtype, nullptr, cfg->act, st),
+                  "gemm launch");
+}
+
+// ---- The entry point that allocates nothing: its workspace is `scratch`, a file-scope device
+// array (one copy per GPU, held until the process ends). Host code never passes the array's
+// name to a kernel: it is a host-side stand-in there. Its device address is looked up once per
+// device with hipGetSymbolAddress, with that device current, and cached here.
+__device__ __align__(256) uint8_t scratch[RQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+rq_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return from_hip(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(RQ_EUNSUPPORTED, "device %d (the static scratch serves devices 0..%d)", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return from_hip(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(RQ_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
   return ok();
 }
 
@@ -269,21 +341,27 @@ rq_status rq_rotq_linear(const void* X, int32_t x_dtype, int64_t M, int64_t K, c
                          void* stream) {
   rq_status s = check_linear(X, x_dtype, M, K, Wq, w_scale, N, bias, cfg, Y, workspace, ws_bytes);
   if (s || M == 0) return s;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  // The workspace holds the codes in the tiled layout (FP6 tiles with FP6 weights), then x_scale.
-  const int32_t xl = fused_x_layout(cfg);
-  uint8_t* Xq = static_cast<uint8_t*>(workspace);
-  float* sx = reinterpret_cast<float*>(Xq + round256(x_code_bytes(M, K, cfg->bits, xl)));
-  if ((s = from_hip(convrot::launch_rotate_quant(X, x_dtype, M, K, cfg->bits, code_layout(xl), Xq, sx, st),
-                    "rotate_quant launch")))
-    return s;
-  if (xl == RQ_X_FP6)
-    return from_hip(convrot::launch_gemm_fp6(Xq, sx, Wq, w_scale, bias, M, N, K, Y, x_dtype, nullptr,
-                                             cfg->act, st),
-                    "gemm launch");
-  return from_hip(convrot::launch_gemm(Xq, sx, Wq, w_scale, bias, M, N, K, cfg->bits, true, Y,
-                                       x_dtype, nullptr, cfg->act, st),
-                  "gemm launch");
+  return launch_linear(X, x_dtype, M, K, Wq, w_scale, N, bias, cfg, Y, workspace,
+                       static_cast<hipStream_t>(stream));
+}
+
+rq_status rq_rotq_linear_noalloc(const void* X, int32_t x_dtype, int64_t M, int64_t K,
+                                 const void* Wq, const float* w_scale, int64_t N, const float* bias,
+                                 const rq_qconfig* cfg, void* Y, void* stream) {
+  // The size limit first, so that an oversized call gets this status whatever its pointers.
+  rq_status s = check_cfg(cfg);
+  if (s) return s;
+  if ((s = check_gemm_shape(M, N, K))) return s;
+  const size_t need = rq_rotq_linear_workspace_size(M, K, cfg);
+  if (need > (size_t)RQ_NOALLOC_SCRATCH_BYTES)
+    return fail(RQ_EWORKSPACE, "the call needs %zu bytes of workspace; the static scratch holds %zu "
+                               "(use rq_rotq_linear with a caller workspace)",
+                need, (size_t)RQ_NOALLOC_SCRATCH_BYTES);
+  if ((s = check_linear_core(X, x_dtype, M, K, Wq, w_scale, N, bias, cfg, Y)) || M == 0) return s;
+  void* ws = nullptr;
+  if ((s = scratch_of_current_device(&ws))) return s;
+  if ((s = check_linear_ws(X, M, K, Wq, w_scale, N, bias, cfg, Y, ws, RQ_NOALLOC_SCRATCH_BYTES))) return s;
+  return launch_linear(X, x_dtype, M, K, Wq, w_scale, N, bias, cfg, Y, ws, static_cast<hipStream_t>(stream));
 }
 
 rq_status rq_gemm_dequant(const void* Xq, const float* x_scale, const void* Wq,
