@@ -70,6 +70,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rw_rsrc(const void* base, uint
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8):
+// vmcnt(n) with lgkmcnt(0), or vmcnt(n) alone.
+constexpr int vm_lgkm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
+constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
 // NT n-tiles per XCD times G row groups = 32 workgroups per XCD; rb_total 64-token blocks.
 // The per-wave loop body (16 k steps and the epilogue) is one basic block: stores and the
 // x_scale loads are buffer operations whose out-of-range lanes the hardware drops (stores) or
@@ -103,13 +108,29 @@ __global__ __launch_bounds__(kRwThreads, 1) void gemm_rw_kernel(
 
   // 1. The n-tile's weights into LDS, fragment f = kk * NA + a at f * 1 KB: lane l holds row
   //    n0 + 16 a + l % 16, bytes 64 kk + 16 (l / 16) .. +16. Rows past N re-read the last row.
+  //    Wave w copies fragments w + 8 i in increasing i, so its first half of the copies holds
+  //    k steps 0..7 (fragments 0..47) and its second half k steps 8..15. The workgroup starts
+  //    multiplying once the first half has landed; the first block waits for the second half
+  //    (and passes a second barrier) before it reads the weights of k step 8.
+  constexpr int kFrags = NA * NK;
+  constexpr int kFillPerWave = kFrags / kRwWaves;             // 12 copies per wave
+  static_assert(kFrags % kRwWaves == 0 && kFillPerWave % 2 == 0 &&
+                    kRwWaves * (kFillPerWave / 2) == NA * (NK / 2),
+                "each wave's first half of copies is exactly k steps 0..NK/2-1");
   {
+    float my_sw = 0.0f, my_b = 0.0f;
+    if constexpr (OUT != kOutS32) {
+      // Issued before the copies, so that parking them in LDS waits for these loads only.
+      if ((int)threadIdx.x < BN) {
+        const int n = n0 + (int)threadIdx.x;
+        my_sw = n < N ? sw[n] : 0.0f;
+        my_b = (n < N && bias) ? bias[n] : 0.0f;
+      }
+    }
     const int wrows = N - n0 < BN ? N - n0 : BN;
     const __amdgpu_buffer_rsrc_t wrs = rw_rsrc(Wq + (int64_t)n0 * Kb, (uint32_t)wrows * Kb);
-    constexpr int kFrags = NA * NK;
-    static_assert(kFrags % kRwWaves == 0, "whole fragments per wave");
 #pragma unroll
-    for (int i = 0; i < kFrags / kRwWaves; i++) {
+    for (int i = 0; i < kFillPerWave; i++) {
       const int f = wave + kRwWaves * i;
       const int kk = f / NA, a = f - kk * NA;
       int r = a * 16 + (lane & 15);
@@ -119,14 +140,16 @@ __global__ __launch_bounds__(kRwThreads, 1) void gemm_rw_kernel(
     }
     if constexpr (OUT != kOutS32) {
       if ((int)threadIdx.x < BN) {
-        const int n = n0 + (int)threadIdx.x;
-        e_sw[threadIdx.x] = n < N ? sw[n] : 0.0f;
-        e_b[threadIdx.x] = (n < N && bias) ? bias[n] : 0.0f;
+        e_sw[threadIdx.x] = my_sw;
+        e_b[threadIdx.x] = my_b;
       }
     }
     if (threadIdx.x == 0) *next_block = rb_lo + kRwWaves;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    // This wave's first half of the copies has landed (the second half may still be in
+    // flight), and so have its LDS writes; then every wave's first half has.
+    __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(kFillPerWave / 2));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // 2. The workgroup's token blocks [rb_lo, rb_hi): wave w starts with block rb_lo + w and then
@@ -134,7 +157,12 @@ __global__ __launch_bounds__(kRwThreads, 1) void gemm_rw_kernel(
   //    more blocks and the workgroup's waves finish together. A wave claims its next block as
   //    it starts the current one, in time to load the next block's first k steps ahead.
   int rb = rb_lo + wave;
-  if (rb >= rb_hi) return;
+  if (rb >= rb_hi) {
+    // Not reached under the launcher's rule (every wave has a first block); a wave without
+    // one still passes the first block's barrier before it leaves.
+    __builtin_amdgcn_s_barrier();
+    return;
+  }
   // One LDS atomic per claim: every lane adds (lane 0 adds 1, the others 0), lane 0's return
   // value is the claimed block. (No branch, so the block loop stays one basic block.)
   auto claim = [&]() __attribute__((always_inline)) {
@@ -195,30 +223,31 @@ __global__ __launch_bounds__(kRwThreads, 1) void gemm_rw_kernel(
     *reinterpret_cast<uint2*>(stage + q * S::kBuf + r16 * S::kPitch + stage_pos(cc, r16) * 16 + (hq & 1) * 8) =
         make_uint2(lo, hi);
   };
-  // Read back buffer q: lane l takes row 4 it + l / 16, chunk l % 16 (chunks 12..15 idle). For
-  // that row 3 (row / 2) = 6 it + 3 (l / 32), so the chunk position (c + 3 (row / 2)) mod 12
-  // takes one of two per-lane values, by the parity of it.
-  const int jc = (lane & 15) < 12 ? (lane & 15) : 11;
-  const int rd_even = (lane >> 4) * S::kPitch + stage_pos(jc, (lane >> 4)) * 16;
-  const int rd_odd = (lane >> 4) * S::kPitch + stage_pos(jc, (lane >> 4) + 4) * 16;
-  auto stage_read = [&](int q, u32x4 (&v)[4]) __attribute__((always_inline)) {
+  // Read back buffer q and store it: the 16 rows x 12 chunks of 16 bytes are 192 chunks, three
+  // full 64-lane instructions; chunk f = 64 it + l is chunk f % 12 of row f / 12. Per-lane
+  // offsets (LDS and output) are computed once; the round's output offset is scalar.
+  int rd_off[3], st_off[3];
 #pragma unroll
-    for (int it = 0; it < 4; it++)
-      v[it] = *reinterpret_cast<const u32x4*>(stage + q * S::kBuf + it * 4 * S::kPitch + ((it & 1) ? rd_odd : rd_even));
+  for (int it = 0; it < 3; it++) {
+    const int f = it * 64 + lane, row = f / 12, j = f - row * 12;
+    rd_off[it] = row * S::kPitch + stage_pos(j, row) * 16;
+    st_off[it] = n0 + j * 8 < N ? (row * N + n0 + j * 8) * 2 : (int)0x80000000;
+  }
+  auto stage_read = [&](int q, u32x4 (&v)[3]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int it = 0; it < 3; it++) v[it] = *reinterpret_cast<const u32x4*>(stage + q * S::kBuf + rd_off[it]);
   };
-  // Output offsets: lane l stores chunk l % 16 of token (row) 4 it + l / 16 of round r; idle
-  // chunks (and features past N) get an offset past every buffer, which the hardware drops.
-  const int st_lane = ((lane & 15) < BN / 8 && n0 + (lane & 15) * 8 < N)
-                          ? ((lane >> 4) * N + n0 + (lane & 15) * 8) * 2 : (int)0x80000000;
-  auto store_round = [&](int r, const u32x4 (&v)[4]) __attribute__((always_inline)) {
+  // Output offsets past every buffer (features past N) are dropped by the hardware, as are
+  // rows past the block's valid tokens (the resource's size).
+  auto store_round = [&](int r, const u32x4 (&v)[3]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int it = 0; it < 4; it++)
-      __builtin_amdgcn_raw_buffer_store_b128(v[it], yrs_prev, st_lane, (r * 16 + it * 4) * N * 2, kStoreAux);
+    for (int it = 0; it < 3; it++)
+      __builtin_amdgcn_raw_buffer_store_b128(v[it], yrs_prev, st_off[it], r * 16 * N * 2, kStoreAux);
   };
   // Round r of the previous block's outputs, in k step r of the next block (or in the flush):
   // before the step's MFMAs, stage it (rounds 2, 3, from pk) and read it back; after them,
   // store it.
-  auto round_read = [&](int r, u32x4 (&v)[4]) __attribute__((always_inline)) {
+  auto round_read = [&](int r, u32x4 (&v)[3]) __attribute__((always_inline)) {
     if (r >= 2) {
 #pragma unroll
       for (int a = 0; a < NA; a++) stage_write(r - 2, a, pk[r - 2][a][0], pk[r - 2][a][1]);
@@ -232,6 +261,7 @@ __global__ __launch_bounds__(kRwThreads, 1) void gemm_rw_kernel(
   // loop head stay as loose as in the loop.
   auto block = [&](int rb, int rb_next, auto prev_tag) __attribute__((always_inline)) {
     constexpr bool PREV = decltype(prev_tag)::value;
+    constexpr bool FIRST = !PREV;                 // the peeled first block of the wave
     // The next block (this one again after the last: harmless in-bounds look-ahead loads).
     const int base_next = block_base(rb_next < rb_hi ? rb_next : rb);
     const int m_base = rb * kRwRows;
@@ -250,13 +280,23 @@ __global__ __launch_bounds__(kRwThreads, 1) void gemm_rw_kernel(
     // the loads across steps, and each DS read follows its block's four MFMAs.
 #pragma unroll
     for (int kk = 0; kk < NK; kk++) {
+      if constexpr (FIRST) {
+        if (kk == NK / 2 - 1) {
+          // Step 7 reads the weights of step 8: wait for this wave's second half of the
+          // copies (vm operations issued after them: the initial look-ahead loads, the
+          // x_scale loads and the first NK/2 - 1 steps' code loads), then for every wave's.
+          __builtin_amdgcn_s_waitcnt(vm_wait(4 * kRwDepth + 4 + 4 * (NK / 2 - 1)));
+          __builtin_amdgcn_s_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
       const int ahead = kk + kRwDepth;
       if (ahead < NK) {
         load_step(base, ahead, xs[ahead & (kRwSets - 1)]);
       } else {
         load_step(base_next, ahead - NK, xs[ahead & (kRwSets - 1)]);
       }
-      u32x4 vr[4];
+      u32x4 vr[3];
       if constexpr (PREV && OUT != kOutS32) {
         if (kk < 4) round_read(kk, vr);
       }
@@ -337,7 +377,7 @@ __global__ __launch_bounds__(kRwThreads, 1) void gemm_rw_kernel(
   if constexpr (OUT != kOutS32) {
 #pragma unroll
     for (int r = 0; r < 4; r++) {
-      u32x4 vr[4];
+      u32x4 vr[3];
       round_read(r, vr);
       store_round(r, vr);
     }
