@@ -47,7 +47,8 @@ def log(msg):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("gemm_common.h", "gemm_i8.hip", "gemm_i8_wide.hip", "gemm_fp6.hip", "rotate_quant.hip"):
+    for f in ("gemm_common.h", "gemm_i8.hip", "gemm_rw.hip", "gemm_i8_wide.hip", "gemm_fp6.hip",
+              "rotate_quant.hip"):
         with open(os.path.join(ROOT, "w4a4_integer_quantized_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -122,6 +123,22 @@ def gemm_kernel_name(M, N, K, bits, x_layout, w_layout=0, act=0, s32=False):
     if tiles > 256 and Kb >= 3072:
         return "gemm_n2_kernel"
     return "gemm_kernel"
+
+
+def rq_kernel_name(K, fp6=False):
+    """The rotate+quantize kernel the launcher picks, by the dispatch rule of rotate_quant.hip:
+    the coalesced kernel when nb = K / 128 blocks split as G * NI with G in {1, 2, 4, 8, 12, 16}
+    and NI <= 4 (int codes only), else the quad kernel, else the generic one."""
+    nb = K // 128
+    if not fp6 and any(nb % g == 0 and nb // g <= 4 for g in (1, 2, 4, 8, 12, 16)):
+        return "rotate_quant_coalesced_kernel"
+    for bpq in range(1, 5):
+        if nb % bpq:
+            continue
+        lanes = 4 * (nb // bpq)
+        if lanes <= 64 or (lanes % 64 == 0 and lanes <= 256):
+            return "rotate_quant_kernel"
+    return "rotate_quant_generic_kernel"
 
 
 def mfma_summary(counter_csv, trace_csv, n_simd=1024, n_xcc=8):
@@ -360,6 +377,40 @@ def library_int8_gemm(torch, M, N, K, reps=20):
             "out": "int32, no epilogue", "via": "torch._int_mm (hipBLASLt)"}
 
 
+def hbm_ceilings(torch, M, K, reps=20):
+    """Context for the rotate+quantize roofline: what plain PyTorch elementwise kernels reach on
+    the same [M, K] fp16 activation on this GPU, in algorithmic GB/s (each over a ring of
+    buffers larger than the Infinity Cache): the same 2:1 read:write mix as rotate+quantize
+    (fp16 -> int8 conversion), a 1:1 copy, read-only (a sum) and write-only (a fill)."""
+    R = 4
+    xs = [torch.randn((M, K), device="cuda").half() for _ in range(R)]
+    q = [torch.empty((M, K), dtype=torch.int8, device="cuda") for _ in range(R)]
+    h = [torch.empty((M, K), dtype=torch.float16, device="cuda") for _ in range(R)]
+    out = {}
+
+    def timed(name, fn, nbytes):
+        for i in range(3):
+            fn(i % R)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            fn(i % R)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        out[name] = {"us": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                     "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+
+    timed("f16_to_int8_2to1", lambda i: q[i].copy_(xs[i]), M * K * 3)
+    timed("f16_copy_1to1", lambda i: h[i].copy_(xs[i]), M * K * 4)
+    timed("read_only_sum", lambda i: xs[i].sum(dtype=torch.float32), M * K * 2)
+    timed("write_only_fill", lambda i: q[i].fill_(1), M * K)
+    out["shape"] = [M, K]
+    out["via"] = "torch elementwise kernels (context, not targets)"
+    return out
+
+
 def gpu_state():
     """rocm-smi's view of clocks and power right after the timed work (context)."""
     import shutil
@@ -569,6 +620,7 @@ class WorkloadRun:
                 "M": M, "N": lin.N, "K": lin.K,
                 "gemm_kernel": gemm_kernel_name(M, lin.N, lin.K, bits, self.xl, self.wl, self.act_of[lin.name]),
                 "act": self.act_of[lin.name],
+                "rotate_quant_kernel": rq_kernel_name(lin.K, fp6=self.wl != 0),
                 "rotate_quant_us": round(rq_ms * 1e3, 2),
                 "rotate_quant_GBps": round(rq_bytes / (rq_ms * 1e-3) / 1e9, 1),
                 "rotate_quant_hbm_frac": round(rq_bytes / (rq_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
@@ -654,7 +706,7 @@ def main():
                 "alg_bytes_per_launch": dc["gemm_alg_bytes"], "traffic_detail": tr}
     rtr = traffic_from_counters(cfg.workload, "rotate_quant")
     rq_traffic = rtr["bytes"] if rtr else None
-    roofline_rq = {"bound": "hbm", "kernel": "rotate_quant_kernel (%s input %dx%d)" % (dom.name, M, dom.K),
+    roofline_rq = {"bound": "hbm", "kernel": "%s (%s input %dx%d)" % (rq_kernel_name(dom.K), dom.name, M, dom.K),
                    "achieved": dc["rotate_quant_GBps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                    "frac": dc["rotate_quant_hbm_frac"], "traffic": rq_traffic,
                    "avg_launch_us": dc["rotate_quant_us"], "alg_bytes_per_launch": dc["rotate_quant_alg_bytes"],
@@ -713,6 +765,8 @@ def main():
         out["workloads"] = others
 
     if not args.no_context:
+        log("HBM ceilings of plain elementwise kernels on X's shape (context)")
+        out["context_hbm_ceilings"] = hbm_ceilings(torch, M, cfg.K)
         log("library int8 GEMM on the %s shape (context)" % dom.name)
         out["context_library_int8_gemm"] = library_int8_gemm(torch, M, dom.N, dom.K)
         log("offline weight quantizer rules on %s" % dom.name)

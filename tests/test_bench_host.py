@@ -126,3 +126,14 @@ def test_gemm_kernel_label_follows_the_launch_rule():
     assert bench.gemm_kernel_name(2048, 6144, 1536, 8, R) == "gemm_wide_kernel"
     assert bench.gemm_kernel_name(2048, 6144, 1536, 8, R, act=1) == "gemm_kernel"
     assert bench.gemm_kernel_name(257, 512, 4096, 4, rq.RQ_X_FP6, rq.RQ_W_FP6) == "gemm_fp6_kernel"
+
+
+def test_rotate_quant_kernel_label_follows_the_launch_rule():
+    # nb = K / 128 blocks: G * NI with G in {1, 2, 4, 8, 12, 16}, NI <= 4 -> the coalesced kernel
+    for K in (128, 256, 512, 1024, 1536, 2048, 3072, 4096, 6144, 8192):
+        assert bench.rq_kernel_name(K) == "rotate_quant_coalesced_kernel", K
+    for K in (640, 896, 1152, 1280, 1408, 1664, 1792, 1920):   # nb = 5, 7, 9, 10, 11, 13, 14, 15
+        assert bench.rq_kernel_name(K) == "rotate_quant_kernel", K
+    assert bench.rq_kernel_name(17 * 128) == "rotate_quant_generic_kernel"
+    assert bench.rq_kernel_name(1024, fp6=True) == "rotate_quant_kernel"
+    assert bench.rq_kernel_name(80 * 128) == "rotate_quant_generic_kernel"

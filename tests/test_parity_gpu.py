@@ -29,10 +29,13 @@ def _rows(seed, M, K, io, zero_rows=(), dist="normal"):
     return synth.to_io_bits(x, io), None
 
 
-# (K, M) pairs cover every kernel shape: T = 16/32/64/128/256 threads per row, P = 1..8
-# pieces, and the generic two-pass kernel (K = 2176, 17 blocks); M spans ragged tails.
-RQ_CASES = [(128, 1), (128, 37), (256, 5), (384, 33), (640, 9), (1024, 300), (1536, 129),
-            (2176, 11), (4096, 70), (6144, 19), (8192, 6), (16384, 3)]
+# (K, M) pairs cover every kernel shape. Coalesced kernel (nb = K / 128 = G * NI): G = 1 with
+# NI = 1..4 (K = 128 .. 512), G = 2 (768, 1024), G = 4 (1536, 2048), G = 8 (3072, 4096, two waves
+# per row), G = 12 (4608, 6144), G = 16 (8192); the quad kernel (K = 640: 5 blocks, K = 16384:
+# four waves per row); the generic two-pass kernel (K = 2176, 17 blocks). M spans ragged tails.
+RQ_CASES = [(128, 1), (128, 37), (256, 5), (384, 33), (512, 23), (640, 9), (768, 17),
+            (1024, 300), (1536, 129), (2048, 41), (2176, 11), (3072, 13), (4096, 70), (4608, 5),
+            (6144, 19), (8192, 6), (16384, 3)]
 
 
 @pytest.mark.parametrize("K,M", RQ_CASES)
@@ -48,8 +51,8 @@ def test_rotate_quantize_parity(K, M, io, bits):
     assert np.array_equal(xs.cpu().numpy().view(np.uint32), ref_s.view(np.uint32))
 
 
-@pytest.mark.parametrize("K,M", [(128, 1), (384, 33), (1024, 300), (1536, 257), (2176, 11),
-                                 (4096, 70), (6144, 19)])
+@pytest.mark.parametrize("K,M", [(128, 1), (128, 529), (384, 33), (640, 9), (1024, 300),
+                                 (1536, 257), (2176, 11), (3072, 13), (4096, 70), (6144, 19)])
 @pytest.mark.parametrize("io,bits", [("f16", 8), ("bf16", 8), ("f16", 4)])
 def test_rotate_quantize_tiled_layout(K, M, io, bits):
     """The tiled activation-code layout holds exactly the row-major codes (and the oracle's)."""

@@ -7,29 +7,42 @@
 // dynamic per-token quantization). The arithmetic is fixed bit for bit (see convrot.h).
 //
 // Work layout (HBM-bound: one read of X, one write of the codes).
-//   * A 4-lane quad owns a 128-block; lane t (0..3) of the quad holds the 32 consecutive
-//     elements 32*t .. 32*t + 31 as 4 pieces of 8, so element 32*t + 8*i + r of the block has
-//     its bits r (h = 1, 2, 4) and i (h = 8, 16) inside the lane and only t (h = 32, 64)
-//     across lanes. Each lane then stores its 32 codes as one contiguous run (16-byte stores),
-//     which measured faster than interleaving the quad's pieces.
-//   * A row of nb blocks is owned by QPR = nb / BPQ quads, each holding BPQ blocks (block
-//     beta*QPR + q for quad q). Few values per lane (BPQ = 1 where possible) keep registers low
-//     and many waves resident, which is what hides the memory latency. A row takes a slot of
-//     L lanes: the next power of two of 4*QPR when that fits a wave (idle quads re-read a valid
-//     block, are left out of the absmax and store nothing), else exactly 4*QPR = 128..256 lanes
-//     over 2..4 waves that combine their absmax through LDS.
-//   * Butterfly stages in the fixed order h = 1, 2, 4, 8, 16 (in-lane), 32, 64 (DPP quad_perm). For fp16 input the first stage also does the exact upcast: fma(x0, +-1, x1)
-//     on the two halves of a dword (v_fma_mix_f32) is the single fp32 rounding of x0 +- x1.
-//   * Sign tracking in the two cross-lane stages: each lane computes mine + m * partner with
+//   * Main kernel (int8 / int4 codes, row-major or tiled; rotate_quant_coalesced_kernel): a
+//     16-lane group covers a 128-block per load, lane u holding the 8-element chunk
+//     c(u) = u ^ (3 * ((u >> 2) & 1)). Element 8c + r of the block has its bits r (h = 1, 2, 4)
+//     inside the lane and its chunk bits (h = 8, 16, 32, 64) across the group; with this
+//     relabelling of lanes, flipping chunk bit k is lane xor 1, 2, 7 or 8, i.e. the DPP
+//     exchanges quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror and row_ror:8, each
+//     fused into one v_fmac_f32. Every load instruction then reads whole consecutive blocks
+//     (fully coalesced, nontemporal: X is read once) and the codes leave as 8-byte (int8) or
+//     4-byte (int4) stores. These stay ordinary stores: the GEMM reads the codes next, and
+//     nontemporal ones (which leave them out of the caches) measured about 45 us slower on the
+//     following 41472 x 3072 x 1024 GEMM. A row of nb blocks takes 16 * G lanes, each lane
+//     holding NI = nb / G <= 4 chunks: few values per lane keep registers low and many waves
+//     resident, which is what hides the memory latency. Loads and stores are buffer operations
+//     with 32-bit offsets from the workgroup's first row; int8 codes are packed by the
+//     rounding add itself (SDWA byte select).
+//   * A second register-resident kernel (rotate_quant_kernel) serves block counts the first
+//     does not take and the FP6 tile layout: a 4-lane quad owns a 128-block, lane t holding the
+//     32 consecutive elements 32*t .. 32*t + 31 (bits r, i in the lane, t across the quad), and
+//     stores its 32 codes as one contiguous run. A row of nb blocks is owned by QPR = nb / BPQ
+//     quads, each holding BPQ blocks; a row takes a slot of L lanes: the next power of two of
+//     4*QPR when that fits a wave (idle quads re-read a valid block, are left out of the absmax
+//     and store nothing), else exactly 4*QPR = 128..256 lanes over 2..4 waves that combine their
+//     absmax through LDS.
+//   * Butterfly stages in the fixed order h = 1, 2, 4, 8, 16, 32, 64. For fp16 input the first
+//     stage also does the exact upcast: fma(x0, +-1, x1) on the two halves of a dword
+//     (v_fma_mix_f32) is the single fp32 rounding of x0 +- x1.
+//   * Sign tracking in the cross-lane stages: each lane computes mine + m * partner with
 //     m = +1 on the lower and -1 on the upper lane of the pair. The upper lane then holds the
 //     negated butterfly difference (fl is sign-symmetric, so this is exact); a lane's values are
-//     then (-1)^popcount(t) times the true ones (the second stage pairs lanes with equal sign
-//     factors), which is folded into the quantizer's multiplier. Absolute values are unaffected.
+//     then (-1)^popcount(j) times the true ones (j: the lane's cross-lane index bits; later
+//     stages pair lanes with equal sign factors), which is folded into the quantizer's
+//     multiplier. Absolute values are unaffected.
 //   * Quantization: p = fl(u * inv) then fl(p + 1.5*2^23), whose low mantissa byte is the
-//     round-half-even code (|p| <= q_max << 2^22), packed with byte permutes.
-// A second, generic kernel (two passes over the row: absmax, then recompute + quantize, one
-// wave per row with 16 lanes per block) covers block counts the register-resident kernel does
-// not take.
+//     round-half-even code (|p| <= q_max << 2^22).
+// A third, generic kernel (two passes over the row: absmax, then recompute + quantize, one
+// wave per row with 16 lanes per block) covers the remaining block counts.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -48,19 +61,28 @@ __device__ __forceinline__ float dpp_f(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), DPP_CTRL, 0xF, 0xF, true));
 }
 
+// 16 bytes at p; NT: a nontemporal load (streamed input that is read exactly once).
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  const u32x4* q = static_cast<const u32x4*>(p);
+  if constexpr (NT) return __builtin_nontemporal_load(q);
+  else return *q;
+}
+
 // 8 consecutive elements -> fp32 (exact upcast).
-template <int DT>
+template <int DT, bool NT = false>
 __device__ __forceinline__ void load8(const void* base, int64_t elem, float (&v)[8]) {
   if constexpr (DT == kF32) {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + elem);
-    uint4 a = p[0], b = p[1];
-    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
-    v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
-    v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
-    v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+    const float* p = static_cast<const float*>(base) + elem;
+    const u32x4 a = load16<NT>(p), b = load16<NT>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      v[i] = __uint_as_float(a[i]);
+      v[4 + i] = __uint_as_float(b[i]);
+    }
   } else {
-    const uint4 a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem);
-    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+    const u32x4 a = load16<NT>(static_cast<const uint16_t*>(base) + elem);
+    const uint32_t w[4] = {a[0], a[1], a[2], a[3]};
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       if constexpr (DT == kF16) {
@@ -157,16 +179,16 @@ __device__ __forceinline__ void bfly_f16(uint32_t w, float& lo, float& hi) {
 }
 
 // Load piece (8 elements) and apply butterfly stage h = 1 (with the upcast).
-template <int DT>
+template <int DT, bool NT = false>
 __device__ __forceinline__ void load_stage1(const void* base, int64_t elem, float (&v)[8]) {
   if constexpr (DT == kF16) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + elem);
+    const u32x4 a = load16<NT>(static_cast<const uint16_t*>(base) + elem);
     bfly_f16(a[0], v[0], v[1]);
     bfly_f16(a[1], v[2], v[3]);
     bfly_f16(a[2], v[4], v[5]);
     bfly_f16(a[3], v[6], v[7]);
   } else {
-    load8<DT>(base, elem, v);
+    load8<DT, NT>(base, elem, v);
 #pragma unroll
     for (int i = 0; i < 8; i += 2) {
       const float a = v[i], b = v[i + 1];
@@ -442,6 +464,267 @@ __global__ __launch_bounds__(256) void rotate_quant_generic_kernel(const void* _
   if (t == 0) S[row] = scale;
 }
 
+// ---- Coalesced register-resident kernel (int8 / int4 codes, row-major or tiled) ----
+// v[r] = partner(v[r]) * m + v[r] on 8 registers, the partner read through DPP (CTRL): one
+// v_fmac_f32 with a DPP source per value, i.e. the single rounding of v +- partner. Each
+// instruction reads only the register it writes, so only the first can follow the VALU write of
+// its source; the leading s_nop covers the DPP read-after-write (and exec-write) wait states.
+#define RQ_FMAC_DPP8(CTRL)                                                                        \
+  asm volatile("s_nop 4\n\t"                                                                      \
+               "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                \
+               "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                \
+               "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                \
+               "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                \
+               "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                \
+               "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                \
+               "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                \
+               "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf"                    \
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),         \
+                 "+v"(v[6]), "+v"(v[7])                                                           \
+               : "v"(m))
+
+// Cross-lane stages h = 8, 16, 32, 64 on a chunk held by lane u of a 16-lane group with chunk
+// index c(u) = u ^ (3 * ((u >> 2) & 1)): flipping bit k of c is lane xor 1, 2, 7, 8, i.e.
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror and row_ror:8. Sign-tracked with
+// m_k = -1 on the lane whose bit k of c is set, as in the quad scheme above.
+__device__ __forceinline__ void stage_h8(float (&v)[8], float m) { RQ_FMAC_DPP8("quad_perm:[1,0,3,2]"); }
+__device__ __forceinline__ void stage_h16(float (&v)[8], float m) { RQ_FMAC_DPP8("quad_perm:[2,3,0,1]"); }
+__device__ __forceinline__ void stage_h32(float (&v)[8], float m) { RQ_FMAC_DPP8("row_half_mirror"); }
+__device__ __forceinline__ void stage_h64(float (&v)[8], float m) { RQ_FMAC_DPP8("row_ror:8"); }
+#undef RQ_FMAC_DPP8
+
+// max(a, |x|, |y|) in one instruction.
+__device__ __forceinline__ float max_abs2(float a, float x, float y) {
+  float r;
+  asm("v_max3_f32 %0, |%1|, |%2|, %3" : "=v"(r) : "v"(x), "v"(y), "v"(a));
+  return r;
+}
+
+// Max over the 16 lanes of a DPP row (the same four exchanges as the stages), each step one
+// v_max_f32 with a DPP source (s_nop 1: the wait states of a DPP read after a VALU write).
+__device__ __forceinline__ float row16_max(float a) {
+  asm volatile("s_nop 1\n\t"
+               "v_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+               "s_nop 1\n\t"
+               "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+               "s_nop 1\n\t"
+               "v_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+               "s_nop 1\n\t"
+               "v_max_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf"
+               : "+v"(a));
+  return a;
+}
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// The int8 codes of 8 values as two dwords: p = fl(u * tinv), then fl(p + 1.5 * 2^23), whose low
+// byte is the code, written straight into byte i of the dword by the add itself (SDWA
+// dst_sel:BYTE_i, the other bytes kept).
+__device__ __forceinline__ u32x2 quant8_i8(const float (&v)[8], float tinv) {
+  const float magic = kRoundMagic;
+  uint32_t d[2];
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    const float p0 = __fmul_rn(v[4 * h], tinv), p1 = __fmul_rn(v[4 * h + 1], tinv);
+    const float p2 = __fmul_rn(v[4 * h + 2], tinv), p3 = __fmul_rn(v[4 * h + 3], tinv);
+    uint32_t w;
+    asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:DWORD"
+        : "=v"(w) : "v"(p0), "v"(magic));
+    asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+        : "+v"(w) : "v"(p1), "v"(magic));
+    asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+        : "+v"(w) : "v"(p2), "v"(magic));
+    asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+        : "+v"(w) : "v"(p3), "v"(magic));
+    d[h] = w;
+  }
+  return u32x2{d[0], d[1]};
+}
+
+// The int4 codes of 8 values, code i in bits 4i .. 4i+3.
+__device__ __forceinline__ uint32_t quant8_i4(const float (&v)[8], float tinv) {
+  uint32_t o = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) o |= (code_bits(v[i], tinv) & 0xFu) << (4 * i);
+  return o;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rq_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+constexpr int kNt = 2;   // buffer-load cache policy: nontemporal (X is streamed once)
+
+// A row of nb = G * NI blocks takes a slot of S = 16 * G lanes: 16-lane group g (0..G-1) holds
+// blocks g, g + G, ..., g + (NI - 1) * G, lane u of the group the chunk c(u) (elements 8c .. 8c+7)
+// of each. So load i of a slot reads G consecutive blocks (256 * G contiguous bytes of fp16/bf16,
+// lanes in a permuted order): fully coalesced, and nontemporal since X is read exactly once.
+// Stages h = 1, 2, 4 run inside a lane, h = 8 .. 64 across the group (stage_h8 .. stage_h64).
+// S = 16, 32 or 64 lanes (R = 256 / S rows per 256-thread workgroup), or S = 128, 192, 256
+// (R = 1 row per workgroup of S threads, the waves combining their absmax through LDS).
+// Loads and stores are buffer operations on resources based at the workgroup's first row (its R
+// rows lie in one 256-row panel of the tiled layout, as R divides 256): 32-bit offsets whose
+// per-load step is uniform, and rows past M read as zeros (their codes are not stored).
+template <int DT, int BITS, int NI, bool TILED>
+__global__ __launch_bounds__(256) void rotate_quant_coalesced_kernel(const void* __restrict__ X,
+                                                                     int64_t M, int K, int S,
+                                                                     uint8_t* __restrict__ Q,
+                                                                     float* __restrict__ scales) {
+  constexpr int kEs = DT == kF32 ? 4 : 2;
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  const bool multi = S > 64;
+  const int lg = __builtin_ctz(multi ? 64 : S);
+  const int R = multi ? 1 : 256 >> lg;              // rows per workgroup
+  const int t = multi ? tid : (tid & (S - 1));
+  const int r = multi ? 0 : tid >> lg;              // row slot within the workgroup
+  const int64_t row0 = (int64_t)blockIdx.x * R;
+  const int64_t row = row0 + r;
+  const bool active = row < M;
+  const int rows_here = (int)(M - row0 < R ? M - row0 : R);
+  const int G = S >> 4;
+  const int g = t >> 4, u = t & 15;
+  const int c = u ^ (3 * ((u >> 2) & 1));
+
+  const __amdgpu_buffer_rsrc_t xrs =
+      rq_rsrc(static_cast<const uint8_t*>(X) + row0 * K * kEs, (uint32_t)(rows_here * K * kEs));
+  const uint32_t xoff = (uint32_t)((r * K + g * 128 + 8 * c) * kEs);
+  const int xstep = G * 128 * kEs;
+  float v[NI][8];
+#pragma unroll
+  for (int i = 0; i < NI; i++) {
+    if constexpr (DT == kF16) {
+      const u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff, i * xstep, kNt));
+      bfly_f16(a[0], v[i][0], v[i][1]);
+      bfly_f16(a[1], v[i][2], v[i][3]);
+      bfly_f16(a[2], v[i][4], v[i][5]);
+      bfly_f16(a[3], v[i][6], v[i][7]);
+    } else {
+      if constexpr (DT == kF32) {
+        const u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff, i * xstep, kNt));
+        const u32x4 b = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff + 16, i * xstep, kNt));
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          v[i][j] = __uint_as_float(a[j]);
+          v[i][4 + j] = __uint_as_float(b[j]);
+        }
+      } else {
+        const u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff, i * xstep, kNt));
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          v[i][2 * j] = __uint_as_float(a[j] << 16);
+          v[i][2 * j + 1] = __uint_as_float(a[j] & 0xFFFF0000u);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const float x0 = v[i][j], x1 = v[i][j + 1];
+        v[i][j] = __fadd_rn(x0, x1);
+        v[i][j + 1] = __fsub_rn(x0, x1);
+      }
+    }
+  }
+  const float m0 = (c & 1) ? -1.0f : 1.0f, m1 = (c & 2) ? -1.0f : 1.0f;
+  const float m2 = (c & 4) ? -1.0f : 1.0f, m3 = (c & 8) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < NI; i++) stages_2_4(v[i]);
+#pragma unroll
+  for (int i = 0; i < NI; i++) stage_h8(v[i], m0);
+#pragma unroll
+  for (int i = 0; i < NI; i++) stage_h16(v[i], m1);
+#pragma unroll
+  for (int i = 0; i < NI; i++) stage_h32(v[i], m2);
+#pragma unroll
+  for (int i = 0; i < NI; i++) stage_h64(v[i], m3);
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NI; i++)
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) amax = max_abs2(amax, v[i][j], v[i][j + 1]);
+  float a = row16_max(amax);
+  if (S >= 32) a = fmaxf(a, __shfl_xor(a, 16, 64));
+  if (S >= 64) a = fmaxf(a, __shfl_xor(a, 32, 64));
+  if (multi) {
+    if ((tid & 63) == 0) red[tid >> 6] = a;
+    __syncthreads();
+    a = red[0];
+    for (int w = 1; w < (S >> 6); w++) a = fmaxf(a, red[w]);
+  }
+  const float qmax = (BITS == 8) ? 127.0f : 7.0f;
+  float tinv, scale;
+  row_scalars(a, qmax, c, tinv, scale);
+  if (active) {
+    // Code byte kb = (block * 128 + 8c) * BITS / 8 of the row; load i is block g + i * G.
+    const int Kb = K * BITS / 8;
+    const int kb0 = (g * 128 + 8 * c) * BITS / 8;
+    uint32_t qbase_rows, qoff;
+    int qstep;
+    if constexpr (TILED) {
+      qbase_rows = 256u * (uint32_t)Kb;           // the panel
+      qoff = (uint32_t)(((kb0 >> 6) << 14) + ((int)(row & 255) << 6) + (kb0 & 63));
+      qstep = (G * 128 * BITS / 8 / 64) << 14;    // k steps per load, times the step stride
+    } else {
+      qbase_rows = (uint32_t)(rows_here * Kb);
+      qoff = (uint32_t)(r * Kb + kb0);
+      qstep = G * 128 * BITS / 8;
+    }
+    uint8_t* const qb = TILED ? Q + (row0 >> 8) * 256 * (int64_t)Kb : Q + row0 * (int64_t)Kb;
+    const __amdgpu_buffer_rsrc_t qrs = rq_rsrc(qb, qbase_rows);
+#pragma unroll
+    for (int i = 0; i < NI; i++) {
+      if constexpr (BITS == 8)
+        __builtin_amdgcn_raw_buffer_store_b64(quant8_i8(v[i], tinv), qrs, qoff, i * qstep, 0);
+      else
+        __builtin_amdgcn_raw_buffer_store_b32(quant8_i4(v[i], tinv), qrs, qoff, i * qstep, 0);
+    }
+    if (t == 0) scales[row] = scale;
+  }
+}
+
+// Slot of the coalesced kernel for nb blocks per row: the smallest G in {1, 2, 4, 8, 12, 16}
+// (S = 16 * G lanes) with nb = G * NI, NI <= 4; {0, 0} when there is none.
+struct RqCoalesced {
+  int G;
+  int NI;
+};
+
+RqCoalesced choose_coalesced(int64_t nb) {
+  const int gs[6] = {1, 2, 4, 8, 12, 16};
+  for (int G : gs)
+    if (nb % G == 0 && nb / G <= 4) return {G, (int)(nb / G)};
+  return {0, 0};
+}
+
+template <int DT, int BITS, int NI, bool TILED>
+hipError_t launch_coalesced_ni(const void* X, int64_t M, int K, int G, uint8_t* Q, float* S,
+                               hipStream_t st) {
+  const int lanes = 16 * G;
+  const int threads = lanes <= 64 ? 256 : lanes;
+  const int rows_per_block = threads / lanes;
+  const int64_t blocks = (M + rows_per_block - 1) / rows_per_block;
+  hipLaunchKernelGGL((rotate_quant_coalesced_kernel<DT, BITS, NI, TILED>), dim3((unsigned)blocks),
+                     dim3(threads), 0, st, X, M, K, lanes, Q, S);
+  return hipGetLastError();
+}
+
+template <int DT, int BITS, bool TILED>
+hipError_t launch_coalesced_t(const void* X, int64_t M, int K, RqCoalesced sh, uint8_t* Q, float* S,
+                              hipStream_t st) {
+  switch (sh.NI) {
+    case 1: return launch_coalesced_ni<DT, BITS, 1, TILED>(X, M, K, sh.G, Q, S, st);
+    case 2: return launch_coalesced_ni<DT, BITS, 2, TILED>(X, M, K, sh.G, Q, S, st);
+    case 3: return launch_coalesced_ni<DT, BITS, 3, TILED>(X, M, K, sh.G, Q, S, st);
+    default: return launch_coalesced_ni<DT, BITS, 4, TILED>(X, M, K, sh.G, Q, S, st);
+  }
+}
+
+template <int DT, int BITS>
+hipError_t launch_coalesced(const void* X, int64_t M, int K, RqCoalesced sh, uint8_t* Q, float* S,
+                            int tiled, hipStream_t st) {
+  return tiled ? launch_coalesced_t<DT, BITS, true>(X, M, K, sh, Q, S, st)
+               : launch_coalesced_t<DT, BITS, false>(X, M, K, sh, Q, S, st);
+}
+
 struct RqShape {
   int bpq;   // blocks per quad; 0 = generic kernel
   int qpr;   // quads per row
@@ -481,6 +764,11 @@ hipError_t launch_bits(const void* X, int64_t M, int K, RqShape sh, uint8_t* Q, 
 template <int DT>
 hipError_t launch_dt(const void* X, int64_t M, int K, int fmt, RqShape sh, uint8_t* Q, float* S,
                      int layout, hipStream_t st) {
+  const RqCoalesced co = choose_coalesced(K / 128);
+  if (fmt != 6 && co.G != 0) {
+    return fmt == 8 ? launch_coalesced<DT, 8>(X, M, K, co, Q, S, layout, st)
+                    : launch_coalesced<DT, 4>(X, M, K, co, Q, S, layout, st);
+  }
   switch (fmt) {
     case 8: return launch_bits<DT, 8>(X, M, K, sh, Q, S, layout, st);
     case 4: return launch_bits<DT, 4>(X, M, K, sh, Q, S, layout, st);
