@@ -141,11 +141,25 @@ def rq_kernel_name(K, fp6=False):
     return "rotate_quant_generic_kernel"
 
 
-def mfma_summary(counter_csv, trace_csv, n_simd=1024, n_xcc=8):
+def dominant_gemm_kernel(key):
+    """Symbol stem of the GEMM kernel that runs the workload's largest linear inside
+    rq_rotq_linear (tiled activation codes), e.g. "gemm_rw_kernel"."""
+    from w4a4_integer_quantized_amd import binding as rq
+    from w4a4_integer_quantized_amd import synth
+    cfg = synth.CONFIGS[key]
+    dom = max(cfg.linears, key=lambda l: l.N * l.K)
+    return gemm_kernel_name(cfg.M, dom.N, dom.K, cfg.bits, rq.RQ_X_TILED).split()[0]
+
+
+def _matches(name, stem):
+    return stem is None or ("::%s<" % stem) in name or name.startswith(stem + "<")
+
+
+def mfma_summary(counter_csv, trace_csv, n_simd=1024, n_xcc=8, gemm_kernel=None):
     """Reduce a rocprofv3 run with --pmc MfmaUtil SQ_VALU_MFMA_BUSY_CYCLES
     SQ_INSTS_VALU_MFMA_MOPS_I8 GRBM_GUI_ACTIVE --kernel-trace to per-launch figures of the GEMM's
-    largest launch: MFMA busy fraction, int8 MFMA ops, GPU-active cycles per XCD and the shader
-    clock they imply over the traced duration."""
+    largest launch (of the kernel `gemm_kernel` names, when given): MFMA busy fraction, int8 MFMA
+    ops, GPU-active cycles per XCD and the shader clock they imply over the traced duration."""
     import csv
     import numpy as np
     dur = {}
@@ -154,7 +168,7 @@ def mfma_summary(counter_csv, trace_csv, n_simd=1024, n_xcc=8):
             dur[int(r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
     rows = {}
     for did, (name, grid, vals) in _read_counter_csv(counter_csv).items():
-        if _is_gemm(name) and did in dur:
+        if _is_gemm(name) and _matches(name, gemm_kernel) and did in dur:
             rows.setdefault(grid, []).append((name, vals, dur[did]))
     grid = max(rows)
     name = rows[grid][0][0]
@@ -185,16 +199,18 @@ def _median_by_group(csv_path, counter, select):
     return {k: (float(np.median(v)), len(v)) for k, v in groups.items()}
 
 
-def pmc_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, out_path=None):
+def pmc_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, out_path=None,
+                gemm_kernel=None):
     """Reduce four rocprofv3 --pmc runs (bench FETCH_SIZE, bench WRITE_SIZE, copy FETCH_SIZE,
-    copy WRITE_SIZE; counters in KiB per dispatch) to bytes per launch of the dominant GEMM and
-    of the rotate+quantize kernel, scaled by what the same counters read for the plain copy of
-    COPY_BYTES. Writes out_path (default profiles/pmc_traffic.json), keyed by the kernel
-    sources' hash, and returns the document."""
+    copy WRITE_SIZE; counters in KiB per dispatch) to bytes per launch of the dominant GEMM (the
+    largest launch of `gemm_kernel`, when given, else of any GEMM) and of the rotate+quantize
+    kernel, scaled by what the same counters read for the plain copy of COPY_BYTES. Writes
+    out_path (default profiles/pmc_traffic.json), keyed by the kernel sources' hash, and returns
+    the document."""
     out_path = out_path or PMC_FILE
     def fam(name):
         if _is_gemm(name):
-            return "gemm"
+            return "gemm" if _matches(name, gemm_kernel) else None
         if "rotate_quant" in name:
             return "rotate_quant"
         return None
@@ -377,37 +393,46 @@ def library_int8_gemm(torch, M, N, K, reps=20):
             "out": "int32, no epilogue", "via": "torch._int_mm (hipBLASLt)"}
 
 
-def hbm_ceilings(torch, M, K, reps=20):
-    """Context for the rotate+quantize roofline: what plain PyTorch elementwise kernels reach on
-    the same [M, K] fp16 activation on this GPU, in algorithmic GB/s (each over a ring of
-    buffers larger than the Infinity Cache): the same 2:1 read:write mix as rotate+quantize
-    (fp16 -> int8 conversion), a 1:1 copy, read-only (a sum) and write-only (a fill)."""
-    R = 4
+def hbm_ceilings(torch, M, K, rq_us=None, reps=20):
+    """Memory ceilings of the rotate+quantize kernel's access pattern on X [M, K] fp16, in
+    algorithmic GB/s: libconvrot_ceiling.so's kernels issue the coalesced kernel's exact loads
+    and stores (tiled code layout) without its arithmetic -- 2:1 (read X, write one byte per
+    element), read-only and write-only -- each over a ring of buffers larger than the
+    Infinity Cache (as the workload's ring). `rq_us`: the rotate+quantize kernel's time on the same shape, reported as a
+    fraction of the 2:1 ceiling."""
+    import ctypes
+    from w4a4_integer_quantized_amd import build as B
+    lib = ctypes.CDLL(B.CEILING_LIB)
+    fn = lib.rqc_hbm_pattern
+    fn.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                   ctypes.c_int, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    R = max(4, math.ceil(3 * MALL_BYTES / (3 * M * K)))      # >= 3x the Infinity Cache per cycle
     xs = [torch.randn((M, K), device="cuda").half() for _ in range(R)]
-    q = [torch.empty((M, K), dtype=torch.int8, device="cuda") for _ in range(R)]
-    h = [torch.empty((M, K), dtype=torch.float16, device="cuda") for _ in range(R)]
+    q = [torch.empty((-(-M // 256) * 256, K), dtype=torch.int8, device="cuda") for _ in range(R)]
+    stream = torch.cuda.current_stream().cuda_stream
     out = {}
-
-    def timed(name, fn, nbytes):
+    for mode, name, nbytes in ((0, "copy_2to1_same_pattern", 3 * M * K), (1, "read_only", 2 * M * K),
+                               (2, "write_only", M * K)):
+        def call(i):
+            assert fn(mode, xs[i % R].data_ptr(), q[i % R].data_ptr(), M, K, 1, stream) == 0
         for i in range(3):
-            fn(i % R)
+            call(i)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(reps):
-            fn(i % R)
+            call(i)
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / reps
         out[name] = {"us": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
                      "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
-
-    timed("f16_to_int8_2to1", lambda i: q[i].copy_(xs[i]), M * K * 3)
-    timed("f16_copy_1to1", lambda i: h[i].copy_(xs[i]), M * K * 4)
-    timed("read_only_sum", lambda i: xs[i].sum(dtype=torch.float32), M * K * 2)
-    timed("write_only_fill", lambda i: q[i].fill_(1), M * K)
     out["shape"] = [M, K]
-    out["via"] = "torch elementwise kernels (context, not targets)"
+    out["via"] = "libconvrot_ceiling.so rqc_hbm_pattern (the coalesced kernel's loads and stores, no arithmetic)"
+    if rq_us:
+        out["rotate_quant_us"] = rq_us
+        out["rotate_quant_vs_2to1_ceiling"] = round(out["copy_2to1_same_pattern"]["us"] / rq_us, 4)
     return out
 
 
@@ -493,7 +518,13 @@ class WorkloadRun:
         x_host = torch.from_numpy(g["x_bits"].view(np.int16)).view(tdt)
         ws_bytes = {lin.name: rq.workspace_size(M, lin.K, bits, w_layout=wl) for lin in cfg.linears}
         set_bytes = x_host.numel() * 2 + sum(M * lin.N * 2 + ws_bytes[lin.name] for lin in cfg.linears)
-        self.R = R = max(min_sets, min(8, math.ceil(3 * MALL_BYTES / set_bytes)))
+        # Enough sets that every kernel, timed alone over the ring, cycles through at least 3x
+        # the Infinity Cache: the smallest per-kernel footprint (rotate+quantize: X and its codes;
+        # GEMM: the codes and Y) sets the count, within 8 GB of device memory.
+        kern_bytes = min(min(M * lin.K * 2 + M * lin.K * bits // 8, M * lin.K * bits // 8 + M * lin.N * 2)
+                         for lin in cfg.linears)
+        cap = max(min_sets, min(256, (8 << 30) // set_bytes))
+        self.R = R = max(min_sets, min(cap, math.ceil(3 * MALL_BYTES / kern_bytes)))
         self.set_bytes = set_bytes
         self.sets = []
         for _ in range(R):
@@ -606,12 +637,32 @@ class WorkloadRun:
         for i in range(steps):
             self.split_step(i, ev[i])
         torch.cuda.synchronize()
+        # Each kernel alone, `steps` back-to-back launches over the buffer ring between two
+        # events on the launch stream: its average launch duration without per-launch event
+        # overhead. rotate+quantize reads X from HBM here as in a step, and this is its roofline
+        # time. The GEMM alone finds its codes out of the caches (written several launches
+        # earlier), unlike in a step, where they were just written by rotate+quantize and sit in
+        # the Infinity Cache: its roofline time is the split steps' event time, and the
+        # cold-codes time is reported beside it.
+        loop_ms = {}
+        for c, lin in enumerate(self.cfg.linears):
+            for kind, idx, fn in (("rq", 2, self.fn_rq), ("gemm", 3, self.fn_gemm)):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(self.stream)
+                st = 0
+                for i in range(steps):
+                    st |= fn(*self.split[i % self.R][c][idx])
+                e1.record(self.stream)
+                torch.cuda.synchronize()
+                if st:
+                    raise self.rq.ConvRotError(st, "kernel loop", self.rq.load().rq_last_error_detail().decode())
+                loop_ms[(lin.name, kind)] = e0.elapsed_time(e1) / steps
         calls = {}
         kern_us = 0.0
         for c, lin in enumerate(self.cfg.linears):
             rq_t = np.array([ev[i][3 * c].elapsed_time(ev[i][3 * c + 1]) for i in range(steps)])
             gm_t = np.array([ev[i][3 * c + 1].elapsed_time(ev[i][3 * c + 2]) for i in range(steps)])
-            rq_ms, gm_ms = float(rq_t.mean()), float(gm_t.mean())
+            rq_ms, gm_ms = loop_ms[(lin.name, "rq")], float(gm_t.mean())
             kern_us += (rq_ms + gm_ms) * 1e3
             ops = 2 * M * lin.N * lin.K
             rq_bytes = M * lin.K * 2 + M * lin.K * bits // 8 + 4 * M
@@ -631,8 +682,14 @@ class WorkloadRun:
                 "call_TOPS": round(ops / ((rq_ms + gm_ms) * 1e-3) / 1e12, 1),
                 "call_int8_peak_frac": round(ops / ((rq_ms + gm_ms) * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
                 "rotate_quant_alg_bytes": rq_bytes, "gemm_alg_bytes": gemm_bytes, "gemm_alg_ops": ops,
-                "rotate_quant_us_p10_p50_p90": [round(float(np.percentile(rq_t, p)) * 1e3, 2) for p in (10, 50, 90)],
-                "gemm_us_p10_p50_p90": [round(float(np.percentile(gm_t, p)) * 1e3, 2) for p in (10, 50, 90)],
+                "gemm_us_codes_not_cached": round(loop_ms[(lin.name, "gemm")] * 1e3, 2),
+                "timing": "rotate_quant_us: back-to-back launches of the kernel alone; gemm_us: HIP events "
+                          "around the GEMM in split steps (right after its rotate+quantize); split_*: "
+                          "HIP events around each kernel of a split step",
+                "split_rotate_quant_us_mean_p10_p50_p90": [round(float(rq_t.mean()) * 1e3, 2)] + [
+                    round(float(np.percentile(rq_t, p)) * 1e3, 2) for p in (10, 50, 90)],
+                "split_gemm_us_mean_p10_p50_p90": [round(float(gm_t.mean()) * 1e3, 2)] + [
+                    round(float(np.percentile(gm_t, p)) * 1e3, 2) for p in (10, 50, 90)],
             }
         return {"ms_per_step": ms_per_step, "tops": tops, "calls": calls,
                 "kernel_us_per_step": round(kern_us, 2)}
@@ -663,10 +720,11 @@ def main():
                     help="reduce rocprofv3 counter CSVs into profiles/pmc_traffic.json (no GPU)")
     args = ap.parse_args()
     if args.mfma_summary:
-        mfma_summary(*args.mfma_summary)
+        mfma_summary(*args.mfma_summary, gemm_kernel=dominant_gemm_kernel(args.workload))
         return
     if args.pmc_summary:
-        pmc_summary(synth_workload_name(args.workload), *args.pmc_summary)
+        pmc_summary(synth_workload_name(args.workload), *args.pmc_summary,
+                    gemm_kernel=dominant_gemm_kernel(args.workload))
         return
     if args.copy_calibration:
         copy_calibration()
@@ -766,7 +824,7 @@ def main():
 
     if not args.no_context:
         log("HBM ceilings of plain elementwise kernels on X's shape (context)")
-        out["context_hbm_ceilings"] = hbm_ceilings(torch, M, cfg.K)
+        out["context_hbm_ceilings"] = hbm_ceilings(torch, M, cfg.K, rq_us=out["roofline_rotate_quant"]["avg_launch_us"])
         log("library int8 GEMM on the %s shape (context)" % dom.name)
         out["context_library_int8_gemm"] = library_int8_gemm(torch, M, dom.N, dom.K)
         log("offline weight quantizer rules on %s" % dom.name)

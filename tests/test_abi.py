@@ -286,3 +286,22 @@ def test_noalloc_scratch_size_matches_the_header():
     for cfg in synth.CONFIGS.values():
         for lin in cfg.linears:
             assert rq.workspace_size(cfg.M, lin.K, cfg.bits) <= rq.RQ_NOALLOC_SCRATCH_BYTES, (cfg.key, lin.name)
+
+
+def test_ceiling_probe_library_loads_and_rejects_bad_arguments():
+    """The bench's memory-ceiling probe (libconvrot_ceiling.so): exported, and invalid arguments
+    are refused before anything touches a device."""
+    import ctypes
+    from w4a4_integer_quantized_amd import build as B
+    if not os.path.exists(B.CEILING_LIB):
+        pytest.skip("libconvrot_ceiling.so not built")
+    fn = ctypes.CDLL(B.CEILING_LIB).rqc_hbm_pattern
+    fn.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                   ctypes.c_int, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    p = ctypes.c_void_p(16)
+    assert fn(3, p, p, 8, 1024, 1, None) == 1           # unknown mode
+    assert fn(0, None, p, 8, 1024, 1, None) == 1        # null input
+    assert fn(0, p, p, 0, 1024, 1, None) == 1           # empty
+    assert fn(0, p, p, 8, 1000, 1, None) == 1           # K not a multiple of 128
+    assert fn(0, p, p, 8, 17 * 128, 1, None) == 1       # 17 blocks: not G * NI

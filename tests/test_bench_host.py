@@ -116,6 +116,8 @@ def test_gemm_kernel_label_follows_the_launch_rule():
     assert bench.gemm_kernel_name(4033, 3072, 1024, 8, T) == "gemm_rw_kernel"
     assert bench.gemm_kernel_name(4032, 3072, 1024, 8, T) == "gemm_xr_kernel"
     assert bench.gemm_kernel_name(41472, 1024, 1024, 8, T) == "gemm_xr_kernel"
+    assert bench.gemm_kernel_name(8193, 1024, 1024, 8, T) == "gemm_xr_kernel"
+    assert bench.gemm_kernel_name(8128, 1024, 1024, 8, T).startswith("gemm_kernel (8 waves")
     assert bench.gemm_kernel_name(4100, 2064, 1024, 8, T) == "gemm_xr_kernel"
     assert bench.gemm_kernel_name(4100, 2064, 1024, 8, T, s32=True) == "gemm_xr_kernel"   # same kernel for int32
     assert bench.gemm_kernel_name(4100, 2064, 2048, 4, T) == "gemm_kernel"        # int4: Kb = 1024
@@ -137,3 +139,21 @@ def test_rotate_quant_kernel_label_follows_the_launch_rule():
     assert bench.rq_kernel_name(17 * 128) == "rotate_quant_generic_kernel"
     assert bench.rq_kernel_name(1024, fp6=True) == "rotate_quant_kernel"
     assert bench.rq_kernel_name(80 * 128) == "rotate_quant_generic_kernel"
+
+
+def test_summaries_pick_the_dominant_gemm_kernel_by_name(tmp_path):
+    # The persistent resident-weight GEMM has a smaller grid than the other linear's GEMM: the
+    # dominant launch is chosen by kernel name, not by grid size.
+    assert bench.dominant_gemm_kernel("vit_attn") == "gemm_rw_kernel"
+    rw = "void convrot::(anonymous namespace)::gemm_rw_kernel<1, 96, 0>(unsigned char const*)"
+    xr = "void convrot::(anonymous namespace)::gemm_xr_kernel<1, 16>(unsigned char const*)"
+    gib_kib = (1 << 30) / 1024.0
+    cf = _counters(tmp_path / "cf.csv", [(1, 4096, COPY, "FETCH_SIZE", gib_kib)])
+    cw = _counters(tmp_path / "cw.csv", [(1, 4096, COPY, "WRITE_SIZE", gib_kib)])
+    f = _counters(tmp_path / "f.csv", [(1, 131072, rw, "FETCH_SIZE", 100.0), (2, 331776, xr, "FETCH_SIZE", 7.0)])
+    w = _counters(tmp_path / "w.csv", [(1, 131072, rw, "WRITE_SIZE", 200.0), (2, 331776, xr, "WRITE_SIZE", 9.0)])
+    doc = bench.pmc_summary("wl", f, w, cf, cw, out_path=str(tmp_path / "p.json"), gemm_kernel="gemm_rw_kernel")
+    assert doc["workloads"]["wl"]["gemm"]["grid_threads"] == 131072
+    doc = bench.pmc_summary("wl", f, w, cf, cw, out_path=str(tmp_path / "q.json"))
+    assert doc["workloads"]["wl"]["gemm"]["grid_threads"] == 331776
+    assert not bench._matches(rw, "gemm_kernel") and bench._matches(GEMM, "gemm_kernel")

@@ -282,8 +282,12 @@ def test_gemm_xr_choice_parity(M, N, K, bits, layout):
 # the smallest such M, ragged M (a partial last block and a partial last 256-row panel), M just
 # below the threshold (the next kernel takes it), and several blocks per wave. Every element of
 # the int32 accumulators and of both output types is compared.
+# Resident-weight kernel (N = 3072 in 96-feature n-tiles; at least 64 token blocks) at ragged M,
+# the first M below its threshold, and N = 1024 shapes around the split-K kernel's threshold
+# (256 tiles), which the other kernels take.
 RW_CASES = [(4096, 3072, 1024), (4100, 3072, 1024), (4033, 3072, 1024), (9999, 3072, 1024),
-            (4032, 3072, 1024)]
+            (4032, 3072, 1024), (8192, 1024, 1024), (8193, 1024, 1024), (8129, 1024, 1024),
+            (12345, 1024, 1024), (8128, 1024, 1024)]
 
 
 @pytest.mark.parametrize("M,N,K", RW_CASES)

@@ -17,6 +17,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libconvrot.so")
+# Measurement support for bench.py (memory ceilings of the rotate+quantize access pattern);
+# a separate library, not part of libconvrot.so's ABI.
+CEILING_SOURCE = "hbm_ceiling.hip"
+CEILING_LIB = os.path.join(PKG, "libconvrot_ceiling.so")
 BUILD = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
@@ -39,17 +43,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build() -> str:
-    """Compile every HIP source for gfx950 and link libconvrot.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib):
+    tmp = lib + ".tmp%d" % os.getpid()
     r = subprocess.run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build() -> str:
+    """Compile every HIP source for gfx950, link libconvrot.so (and the bench's
+    libconvrot_ceiling.so); returns the path of libconvrot.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
+        objs = list(ex.map(_compile, SOURCES + [CEILING_SOURCE]))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], CEILING_LIB)
     return LIB
 
 

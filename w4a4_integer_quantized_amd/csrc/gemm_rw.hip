@@ -284,8 +284,10 @@ __global__ __launch_bounds__(kRwThreads, 1) void gemm_rw_kernel(
         if (kk == NK / 2 - 1) {
           // Step 7 reads the weights of step 8: wait for this wave's second half of the
           // copies (vm operations issued after them: the initial look-ahead loads, the
-          // x_scale loads and the first NK/2 - 1 steps' code loads), then for every wave's.
-          __builtin_amdgcn_s_waitcnt(vm_wait(4 * kRwDepth + 4 + 4 * (NK / 2 - 1)));
+          // x_scale loads when there is an epilogue, and the first NK/2 - 1 steps' code
+          // loads), then for every wave's.
+          constexpr int kAfter = 4 * kRwDepth + (OUT != kOutS32 ? 4 : 0) + 4 * (NK / 2 - 1);
+          __builtin_amdgcn_s_waitcnt(vm_wait(kAfter));
           __builtin_amdgcn_s_barrier();
           __builtin_amdgcn_sched_barrier(0);
         }
