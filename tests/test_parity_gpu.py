@@ -30,9 +30,10 @@ def _rows(seed, M, K, io, zero_rows=(), dist="normal"):
 
 
 # (K, M) pairs cover every kernel shape. Coalesced kernel (nb = K / 128 = G * NI): G = 1 with
-# NI = 1..4 (K = 128 .. 512), G = 2 (768, 1024), G = 4 (1536, 2048), G = 8 (3072, 4096, two waves
-# per row), G = 12 (4608, 6144), G = 16 (8192); the quad kernel (K = 640: 5 blocks, K = 16384:
-# four waves per row); the generic two-pass kernel (K = 2176, 17 blocks). M spans ragged tails.
+# NI = 1..4 (K = 128 .. 512), G = 2 (768, 1024), G = 4 (1536, 2048), G = 12 (3072, 4608; three
+# waves per row), G = 16 (4096, 6144, 8192; four waves per row); the quad kernel (K = 640:
+# 5 blocks, K = 16384: four waves per row); the generic two-pass kernel (K = 2176, 17 blocks).
+# M spans ragged tails.
 RQ_CASES = [(128, 1), (128, 37), (256, 5), (384, 33), (512, 23), (640, 9), (768, 17),
             (1024, 300), (1536, 129), (2048, 41), (2176, 11), (3072, 13), (4096, 70), (4608, 5),
             (6144, 19), (8192, 6), (16384, 3)]

@@ -61,27 +61,22 @@ __device__ __forceinline__ float dpp_f(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), DPP_CTRL, 0xF, 0xF, true));
 }
 
-// 16 bytes at p; NT: a nontemporal load (streamed input that is read exactly once).
-template <bool NT>
-__device__ __forceinline__ u32x4 load16(const void* p) {
-  const u32x4* q = static_cast<const u32x4*>(p);
-  if constexpr (NT) return __builtin_nontemporal_load(q);
-  else return *q;
-}
+// 16 bytes at p.
+__device__ __forceinline__ u32x4 load16(const void* p) { return *static_cast<const u32x4*>(p); }
 
 // 8 consecutive elements -> fp32 (exact upcast).
-template <int DT, bool NT = false>
+template <int DT>
 __device__ __forceinline__ void load8(const void* base, int64_t elem, float (&v)[8]) {
   if constexpr (DT == kF32) {
     const float* p = static_cast<const float*>(base) + elem;
-    const u32x4 a = load16<NT>(p), b = load16<NT>(p + 4);
+    const u32x4 a = load16(p), b = load16(p + 4);
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       v[i] = __uint_as_float(a[i]);
       v[4 + i] = __uint_as_float(b[i]);
     }
   } else {
-    const u32x4 a = load16<NT>(static_cast<const uint16_t*>(base) + elem);
+    const u32x4 a = load16(static_cast<const uint16_t*>(base) + elem);
     const uint32_t w[4] = {a[0], a[1], a[2], a[3]};
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -179,16 +174,16 @@ __device__ __forceinline__ void bfly_f16(uint32_t w, float& lo, float& hi) {
 }
 
 // Load piece (8 elements) and apply butterfly stage h = 1 (with the upcast).
-template <int DT, bool NT = false>
+template <int DT>
 __device__ __forceinline__ void load_stage1(const void* base, int64_t elem, float (&v)[8]) {
   if constexpr (DT == kF16) {
-    const u32x4 a = load16<NT>(static_cast<const uint16_t*>(base) + elem);
+    const u32x4 a = load16(static_cast<const uint16_t*>(base) + elem);
     bfly_f16(a[0], v[0], v[1]);
     bfly_f16(a[1], v[2], v[3]);
     bfly_f16(a[2], v[4], v[5]);
     bfly_f16(a[3], v[6], v[7]);
   } else {
-    load8<DT, NT>(base, elem, v);
+    load8<DT>(base, elem, v);
 #pragma unroll
     for (int i = 0; i < 8; i += 2) {
       const float a = v[i], b = v[i + 1];
@@ -681,8 +676,11 @@ __global__ __launch_bounds__(256) void rotate_quant_coalesced_kernel(const void*
   }
 }
 
-// Slot of the coalesced kernel for nb blocks per row: the smallest G in {1, 2, 4, 8, 12, 16}
-// (S = 16 * G lanes) with nb = G * NI, NI <= 4; {0, 0} when there is none.
+// Slot of the coalesced kernel for nb blocks per row: G in {1, 2, 4, 8, 12, 16} (S = 16 * G
+// lanes) with nb = G * NI, NI <= 4; {0, 0} when there is none. Below 24 blocks the smallest
+// such G (rows within one wave: at K = 1024, 32 lanes per row measured 23.3 us against 30.4 for
+// 128), from 24 blocks the largest (fewer values per lane across more waves: at K = 4096 int8,
+// 16.0 us with 256 lanes per row against 19.4 with 128; at K = 6144, 31.7 against 32.9).
 struct RqCoalesced {
   int G;
   int NI;
@@ -690,8 +688,10 @@ struct RqCoalesced {
 
 RqCoalesced choose_coalesced(int64_t nb) {
   const int gs[6] = {1, 2, 4, 8, 12, 16};
-  for (int G : gs)
+  for (int i = 0; i < 6; i++) {
+    const int G = nb < 24 ? gs[i] : gs[5 - i];
     if (nb % G == 0 && nb / G <= 4) return {G, (int)(nb / G)};
+  }
   return {0, 0};
 }
 
