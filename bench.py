@@ -805,19 +805,25 @@ def main():
     }
     out["gpu_state_after_timing"] = gpu_state()
 
-    # Every other workload, each timed the same way (fewer steps; not part of `value`).
+    # Every other workload, each timed the same way (fewer steps; not part of `value`), and the
+    # 4-bit workload once more on the other code path (FP6 matrix cores, or the int8 ones when
+    # --w4-fp6 made FP6 the default), under the key "<key>_fp6" / "<key>_int8".
     if not args.no_other_workloads:
         others = {}
-        for key in synth.CONFIGS:
-            if key == args.workload:
-                continue
-            other = WorkloadRun(key, stream, w4_fp6=args.w4_fp6, unfused_gelu=args.unfused_gelu)
+        runs = [(key, args.w4_fp6, key) for key in synth.CONFIGS if key != args.workload]
+        runs += [(key, not args.w4_fp6, key + ("_int8" if args.w4_fp6 else "_fp6"))
+                 for key in synth.CONFIGS if synth.CONFIGS[key].bits == 4]
+        for key, fp6, label in runs:
+            other = WorkloadRun(key, stream, w4_fp6=fp6, unfused_gelu=args.unfused_gelu)
             pg = PEAK_FP6_TOPS if other.wl == rq.RQ_W_FP6 else PEAK_INT8_TOPS
             r = other.time(max(20, args.steps // 2), max(5, args.warmup // 2), pg)
-            others[key] = {"workload": other.cfg.workload, "ms_per_step": round(r["ms_per_step"], 4),
-                           "step_TOPS": round(r["tops"], 1),
-                           "step_int8_peak_frac": round(r["tops"] / PEAK_INT8_TOPS, 4),
-                           "kernel_us_per_step": r["kernel_us_per_step"], "calls": r["calls"]}
+            others[label] = {"workload": other.cfg.workload, "ms_per_step": round(r["ms_per_step"], 4),
+                             "step_TOPS": round(r["tops"], 1),
+                             "step_int8_peak_frac": round(r["tops"] / PEAK_INT8_TOPS, 4),
+                             "kernel_us_per_step": r["kernel_us_per_step"],
+                             "four_bit_codes_on": ("fp6 matrix cores" if other.wl == rq.RQ_W_FP6 else
+                                                   "int8 matrix cores") if other.bits == 4 else None,
+                             "calls": r["calls"]}
             del other
             torch.cuda.empty_cache()
         out["workloads"] = others

@@ -30,12 +30,14 @@ def _rows(seed, M, K, io, zero_rows=()):
     return (x if io == "f32" else synth.to_io_bits(x, io)), x
 
 
-@pytest.mark.parametrize("K,M", [(128, 1), (256, 37), (1024, 300), (2176, 11), (4096, 257),
-                                 (6144, 19), (16384, 3)])
+@pytest.mark.parametrize("K,M", [(128, 1), (256, 37), (384, 33), (512, 529), (640, 9), (1024, 300),
+                                 (1536, 129), (2176, 11), (3072, 13), (4096, 257), (6144, 19),
+                                 (16384, 3)])
 @pytest.mark.parametrize("io", ["f16", "bf16", "f32"])
 def test_rotate_quantize_fp6_tiles(K, M, io):
-    """Activation codes as FP6 tiles decode to exactly the oracle's 4-bit codes (fast and generic
-    rotate kernels: K = 2176 takes the generic one)."""
+    """Activation codes as FP6 tiles decode to exactly the oracle's 4-bit codes: the quad kernel,
+    which writes FP6 tiles, at every slot shape it takes (K = 128 .. 16384, ragged M over several
+    256-row panels) and the generic kernel (K = 2176)."""
     need_gpu()
     xb, _ = _rows(K + M, M, K, io, zero_rows=(0,) if M > 1 else ())
     Xt, xs = rq.rotate_quantize(dev_from_bits(xb, io), bits=4, x_layout=rq.RQ_X_FP6)
@@ -48,7 +50,8 @@ def test_rotate_quantize_fp6_tiles(K, M, io):
 
 
 @pytest.mark.parametrize("mode", [rq.RQ_W_ABSMAX, rq.RQ_W_MSE, rq.RQ_W_TENSOR])
-@pytest.mark.parametrize("N,K", [(16, 128), (100, 384), (1024, 4096), (48, 2176)])
+@pytest.mark.parametrize("N,K", [(16, 128), (100, 384), (1024, 4096), (48, 2176), (300, 1024),
+                                 (130, 640)])
 def test_quantize_weights_fp6_tiles(mode, N, K):
     need_gpu()
     rng = np.random.default_rng(N + K + mode)
