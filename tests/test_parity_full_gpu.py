@@ -162,3 +162,45 @@ def test_maximum_k(bits):
     sign = np.where(np.arange(16) % 2 == 0, 1, -1)
     expect = np.stack([sign, -sign, sign]) * (q * q * K)
     assert np.array_equal(acc, expect)
+
+
+def test_rows_beyond_32bit_offsets():
+    """2^21 + 3 token rows of K = 1024 fp16 through rq_rotq_linear with N = 1024: X and Y pass
+    4 GiB and the tiled codes 2 GiB, the sizes at which a 32-bit byte offset from a tensor's start
+    would wrap. The rows on both sides of those boundaries, the first rows and the ragged last
+    panel are checked bit-exact against the oracle: codes and scales (read back from the
+    workspace) and outputs."""
+    need_gpu()
+    M, K, N, bits = (1 << 21) + 3, 1024, 1024, 8
+    print("rows-beyond-32-bit case M=%d K=%d N=%d" % (M, K, N), flush=True)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20)
+    X = torch.randn((M, K), device="cuda", generator=gen).half()
+    rng = np.random.default_rng(21)
+    W = rng.normal(0, 0.02, (N, K)).astype(np.float32)
+    b = rng.normal(0, 0.01, N).astype(np.float32)
+    Wq, ws = rq.quantize_weights(dev_from_bits(W, "f32"), bits=bits)
+    wsbuf = torch.empty((rq.workspace_size(M, K, bits),), dtype=torch.uint8, device="cuda")
+    Y = rq.rotq_linear(X, Wq, ws, torch.from_numpy(b).cuda(), bits=bits, workspace=wsbuf)
+    torch.cuda.synchronize()
+
+    rows = np.array([0, 1, 255, 256, 1 << 20, (1 << 21) - 1, 1 << 21, (1 << 21) + 1, M - 1])
+    rows_d = torch.from_numpy(rows).cuda()
+    xb = X[rows_d].cpu().numpy().view(np.uint16)
+    cb = rq.rq_codes_bytes(M, K, rq.make_cfg(bits, x_layout=rq.RQ_X_TILED))
+    assert cb > (1 << 31) and M * K * 2 > (1 << 32) and M * N * 2 > (1 << 32)
+    # Tiled byte index of (row, byte): ((row / 256 * K / 64 + byte / 64) * 256 + row % 256) * 64
+    # + byte % 64 (the layout of include/convrot.h).
+    m = rows[:, None].astype(np.int64)
+    kb = np.arange(K, dtype=np.int64)[None, :]
+    idx = (((m // 256) * (K // 64) + kb // 64) * 256 + m % 256) * 64 + kb % 64
+    got_codes = wsbuf[torch.from_numpy(idx.reshape(-1)).cuda()].cpu().numpy().view(np.int8).reshape(len(rows), K)
+    xs = wsbuf[_round256(cb):_round256(cb) + 4 * M].view(torch.float32)[rows_d].cpu().numpy()
+    got_y = bits_from_dev(Y[rows_d])
+
+    ref_c, ref_s, ref_p = oracle.quantize_rows(xb, oracle.F16, bits, want_pre=True)
+    assert compare_codes(got_codes, ref_c, ref_p, bits, K) == 0
+    assert np.array_equal(xs.view(np.uint32), ref_s.view(np.uint32))
+    wc, _, wsr = oracle.quantize_weights(W, bits)
+    ref = oracle.rotq_linear(xb, oracle.F16, wc, wsr, b, bits)
+    assert np.array_equal(got_y, ref["Y"])
