@@ -164,14 +164,16 @@ def test_maximum_k(bits):
     assert np.array_equal(acc, expect)
 
 
-def test_rows_beyond_32bit_offsets():
-    """2^21 + 3 token rows of K = 1024 fp16 through rq_rotq_linear with N = 1024: X and Y pass
-    4 GiB and the tiled codes 2 GiB, the sizes at which a 32-bit byte offset from a tensor's start
-    would wrap. The rows on both sides of those boundaries, the first rows and the ragged last
-    panel are checked bit-exact against the oracle: codes and scales (read back from the
-    workspace) and outputs."""
+@pytest.mark.parametrize("M,N", [((1 << 21) + 3, 1024), ((1 << 21) - 256, 3072)])
+def test_rows_beyond_32bit_offsets(M, N):
+    """Over two million token rows of K = 1024 fp16 through rq_rotq_linear. With 2^21 + 3 rows
+    and N = 1024, X and Y pass 4 GiB and the tiled codes 2 GiB, the sizes at which a 32-bit byte
+    offset from a tensor's start would wrap (the 256 x 128 kernel). With 2^21 - 256 rows and
+    N = 3072 (the largest M the resident-weight kernel takes) Y passes 8 GiB. The rows on both
+    sides of those boundaries, the first rows and the last ones are checked bit-exact against the
+    oracle: codes and scales (read back from the workspace) and outputs."""
     need_gpu()
-    M, K, N, bits = (1 << 21) + 3, 1024, 1024, 8
+    K, bits = 1024, 8
     print("rows-beyond-32-bit case M=%d K=%d N=%d" % (M, K, N), flush=True)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(20)
@@ -184,11 +186,15 @@ def test_rows_beyond_32bit_offsets():
     Y = rq.rotq_linear(X, Wq, ws, torch.from_numpy(b).cuda(), bits=bits, workspace=wsbuf)
     torch.cuda.synchronize()
 
-    rows = np.array([0, 1, 255, 256, 1 << 20, (1 << 21) - 1, 1 << 21, (1 << 21) + 1, M - 1])
+    # Rows where X (2 KiB per row), Y (2N bytes per row) or the codes cross 2^31, 2^32, 2^33 bytes.
+    edges = {b // rb for b in (1 << 31, 1 << 32, 1 << 33) for rb in (2 * K, 2 * N, K)}
+    rows = sorted({0, 1, 63, 64, 255, 256, M - 65, M - 64, M - 1} |
+                  {r + d for r in edges for d in (-1, 0, 1) if 0 <= r + d < M})
+    rows = np.array(rows)
     rows_d = torch.from_numpy(rows).cuda()
     xb = X[rows_d].cpu().numpy().view(np.uint16)
     cb = rq.rq_codes_bytes(M, K, rq.make_cfg(bits, x_layout=rq.RQ_X_TILED))
-    assert cb > (1 << 31) and M * K * 2 > (1 << 32) and M * N * 2 > (1 << 32)
+    assert M * N * 2 > (1 << 32)
     # Tiled byte index of (row, byte): ((row / 256 * K / 64 + byte / 64) * 256 + row % 256) * 64
     # + byte % 64 (the layout of include/convrot.h).
     m = rows[:, None].astype(np.int64)
