@@ -65,3 +65,39 @@ def test_noalloc_rejects_calls_beyond_the_scratch():
     st = rq.rq_rotq_linear_noalloc(small.data_ptr(), rq.RQ_F16, 0, K, Wq.data_ptr(), ws.data_ptr(), N,
                                    None, rq.make_cfg(8), Y.data_ptr(), torch.cuda.current_stream().cuda_stream)
     assert st == rq.RQ_OK
+
+
+def test_noalloc_replays_under_graph_capture():
+    """Graph capture is one of the uses the entry point is for: a HIP graph holding one
+    rq_rotq_linear_noalloc call (the resident-weight GEMM's shape; no allocation and no memset
+    inside) is replayed three times, with an eager call on another input, which rewrites the
+    shared scratch, and synchronizations between the replays. Every replay gives the eager
+    result bit for bit."""
+    need_gpu()
+    g = synth.generate("vit_attn", M=8192, with_second_layer=False)
+    cfg_ = g["cfg"]
+    lin = max(cfg_.linears, key=lambda l: l.N)
+    X = dev_from_bits(g["x_bits"], cfg_.io)
+    Wq, ws = rq.quantize_weights(dev_from_bits(g["W"][lin.name], "f32"), bits=cfg_.bits)
+    b = torch.from_numpy(g["bias"][lin.name]).cuda()
+    cfg = rq.make_cfg(cfg_.bits)
+    st, ref = _noalloc(X, Wq, ws, b, cfg, lin.N)          # eager: also resolves the scratch
+    torch.cuda.synchronize()
+    assert st == rq.RQ_OK
+    other = torch.randn((300, lin.K), device="cuda").half()
+
+    Y = torch.empty_like(ref)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        st = rq.rq_rotq_linear_noalloc(X.data_ptr(), rq.RQ_F16, X.shape[0], lin.K, Wq.data_ptr(),
+                                       ws.data_ptr(), lin.N, b.data_ptr(), cfg, Y.data_ptr(),
+                                       torch.cuda.current_stream().cuda_stream)
+    assert st == rq.RQ_OK
+    for rep in range(3):
+        Y.zero_()
+        st_o, _ = _noalloc(other, Wq, ws, b, cfg, lin.N)
+        assert st_o == rq.RQ_OK
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Y.view(torch.int16), ref.view(torch.int16)), rep
